@@ -1,0 +1,241 @@
+/*
+ * dlo.h -- C ABI of the layer-by-layer, weight-streamed DiT forward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (vLLM-Omni "Distributed Layerwise Offload" release page):
+ *   - section "Weight sharding with AllGather reconstruction": each block's
+ *     flattened weight is split into dp_size equal shards of
+ *     ceil(numel / dp_size) elements, zero-padded, and kept in pinned host
+ *     memory; the full layer is rebuilt on the device by an all-gather;
+ *   - section "Double-buffered prefetch with H2D + AllGather overlap": exactly
+ *     two device slots, each the size of the largest block, allocated once;
+ *     block N+1 is copied host-to-device and gathered on side streams while
+ *     block N computes from the other slot; compute waits on an event before
+ *     switching slots; parameters are re-pointed at slices of the slot from
+ *     cached (offset, shape) metadata;
+ *   - section "DP multi-concurrency": waves that cannot run are rejected before
+ *     dispatch and failures close the path instead of hanging it.
+ *
+ * On one GPU this library plays every data-parallel rank: it holds all
+ * dp_size shards of every block, copies all of them host-to-device, and a
+ * reconstruction kernel stands in for all_gather_into_tensor.
+ *
+ * Conventions for every call:
+ *   - the return value is a dlo_status: DLO_OK (0) or a negative error code;
+ *     dlo_last_error() then returns a message (thread-local, valid until the
+ *     next call on the same thread);
+ *   - all validation happens before any GPU work is enqueued; a failed call
+ *     leaves no work in flight;
+ *   - after a HIP error inside dlo_forward or dlo_debug_assemble the context is
+ *     poisoned: every later call on it except dlo_destroy returns
+ *     DLO_E_POISONED (fail closed);
+ *   - a context is not thread-safe; calls on one context must not overlap.
+ *
+ * Data formats:
+ *   - bf16 values travel as their 16-bit patterns (uint16_t);
+ *   - a block's flat weight is the dense concatenation, in this order, of
+ *       Wqkv[3d][d] bqkv[3d] Wo[d][d] bo[d] W1[m][d] b1[m] W2[d][m] b2[d]
+ *       Wada[6d][c] bada[6d] extra_0[..] extra_1[..] ...
+ *     with matrices row-major as [out][in] (y = x W^T + b) and q, k, v the
+ *     three d-row thirds of Wqkv; extra vectors are streamed and reconstructed
+ *     but not read by the block math;
+ *   - activations x are fp32 row-major [tokens][d]; cond is fp32 [c].
+ *
+ * The block math (DiT block with adaLN-Zero conditioning, Peebles & Xie,
+ * "Scalable Diffusion Models with Transformers", section 3.2):
+ *     mod = Wada silu(cond) + bada = (shift1, scale1, gate1, shift2, scale2, gate2)
+ *     x  += gate1 * (attn(LN(x) * (1 + scale1) + shift1) Wo^T + bo)
+ *     x  += gate2 * (gelu_tanh((LN(x) * (1 + scale2) + shift2) W1^T + b1) W2^T + b2)
+ * LayerNorm has no affine parameters and eps 1e-6; attention is non-causal
+ * multi-head softmax(q k^T / sqrt(d / heads)) v.  Between blocks of different
+ * width the residual keeps its first min(d_in, d_out) features and zero-fills
+ * the rest.  GEMM and attention operands are bf16 with fp32 accumulation; the
+ * residual x and the modulation vectors stay fp32.
+ */
+#ifndef DLO_H
+#define DLO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DLO_API __attribute__((visibility("default")))
+#define DLO_ABI_VERSION 1
+
+typedef int32_t dlo_status;
+#define DLO_OK 0
+#define DLO_E_INVAL (-1)     /* bad argument or configuration */
+#define DLO_E_SHAPE (-2)     /* element count or shape does not match the layout */
+#define DLO_E_STATE (-3)     /* call not valid in the context's current state */
+#define DLO_E_HOST_OOM (-4)  /* pinned host allocation failed */
+#define DLO_E_DEV_OOM (-5)   /* the caller's device arena is too small */
+#define DLO_E_HIP (-6)       /* a HIP runtime call failed (context is poisoned) */
+#define DLO_E_POISONED (-7)  /* an earlier HIP error poisoned the context */
+
+/* Context flags (dlo_config.flags). */
+#define DLO_FLAG_TRACE 0x1u        /* record a timed interval per H2D chunk,
+                                      reconstruction chunk and block compute */
+#define DLO_FLAG_SERIALIZE 0x2u    /* test hook: synchronous schedule (copy,
+                                      wait, reconstruct, wait, compute), same
+                                      kernels */
+#define DLO_FLAG_POISON_SLOTS 0x4u /* test hook: fill a slot with bf16 NaN
+                                      before reconstructing into it, so a read
+                                      ahead of the reconstruction shows up */
+
+typedef struct dlo_ctx dlo_ctx;
+
+/* Shape of one block.  d_model must be a multiple of 128 and of n_heads with
+ * d_model / n_heads in {64, 128}; d_mlp a multiple of 128; d_cond a multiple of
+ * 64 and the same for every block.  extra_len lists n_extra lengths (>= 0) of
+ * vectors appended to the flat weight; it is copied by dlo_create. */
+typedef struct dlo_block_desc {
+  int32_t d_model;
+  int32_t n_heads;
+  int32_t d_mlp;
+  int32_t d_cond;
+  int32_t n_extra;
+  int32_t reserved;
+  const int64_t* extra_len;
+} dlo_block_desc;
+
+typedef struct dlo_config {
+  int32_t abi_version;         /* DLO_ABI_VERSION */
+  int32_t num_blocks;          /* >= 1 */
+  const dlo_block_desc* blocks;/* num_blocks entries, copied by dlo_create */
+  int32_t dp_size;             /* number of shards per block, >= 1 */
+  int32_t max_tokens;          /* largest token count dlo_forward accepts, >= 1 */
+  int64_t landing_chunk_elems; /* H2D chunk size in elements; 0 = default
+                                  min(max shard size, 2^24); else >= 4096 */
+  int32_t device;              /* HIP device ordinal the context runs on */
+  uint32_t flags;              /* DLO_FLAG_* */
+  void* arena;                 /* device memory owned by the caller, 256-byte
+                                  aligned, at least dlo_required_bytes' total;
+                                  must stay alive until dlo_destroy */
+  size_t arena_bytes;
+  hipStream_t copy_stream;     /* side stream for H2D copies; NULL = the
+                                  library creates its own */
+  hipStream_t gather_stream;   /* side stream for reconstruction; NULL = the
+                                  library creates its own */
+} dlo_config;
+
+/* One entry of a block's parameter table (cached metadata for re-pointing). */
+typedef struct dlo_param_desc {
+  char name[16];
+  int64_t offset;   /* element offset into the block's flat weight */
+  int32_t ndim;     /* 1 or 2 */
+  int32_t reserved;
+  int64_t shape[2];
+} dlo_param_desc;
+
+/* One timed interval of the streaming schedule (DLO_FLAG_TRACE). */
+#define DLO_IV_H2D 0
+#define DLO_IV_ASM 1
+#define DLO_IV_COMPUTE 2
+typedef struct dlo_interval {
+  int32_t kind;      /* DLO_IV_* */
+  int32_t block;     /* block index */
+  int32_t chunk;     /* chunk index within the block, -1 for compute */
+  int32_t slot;      /* slot written (ASM) or read (COMPUTE), -1 for H2D */
+  int32_t landing;   /* landing buffer written (H2D) or read (ASM), -1 for compute */
+  int32_t reserved;
+  int64_t bytes;     /* bytes moved (H2D, ASM reads) or 0 */
+  double start_ms;   /* relative to the start of the forward */
+  double end_ms;
+} dlo_interval;
+
+typedef struct dlo_stats {
+  int32_t num_blocks;
+  int32_t dp_size;
+  int64_t forwards;            /* completed dlo_forward calls */
+  int64_t max_shard_elems;     /* S_max = max over blocks of ceil(numel_b / dp) */
+  size_t slot_bytes;           /* bytes of ONE slot = 2 * dp * S_max */
+  size_t landing_bytes;        /* both landing buffers */
+  size_t workspace_bytes;      /* activations and scratch */
+  int32_t residency_high_water;/* most blocks resident in slots at once, from
+                                  the last traced forward (0 if untraced) */
+  int32_t n_intervals;         /* intervals recorded by the last traced forward */
+  double last_forward_ms;      /* first H2D start to last compute end (traced) */
+  double sum_h2d_ms;           /* summed busy time per stream (traced) */
+  double sum_asm_ms;
+  double sum_compute_ms;
+  int64_t h2d_bytes_per_forward;
+} dlo_stats;
+
+/* Pure host query: the parameter table, element count and shard size of one
+ * block at dp_size.  out may be NULL (then only counts are returned); cap is
+ * its capacity.  No device or context needed. */
+DLO_API dlo_status dlo_block_layout(const dlo_block_desc* block, int32_t dp_size,
+                                    int64_t* numel, int64_t* shard_size,
+                                    int32_t* n_params, dlo_param_desc* out, int32_t cap);
+
+/* Pure host query, before dlo_create: device bytes the arena must hold.
+ * slots = 2 * slot bytes (the two-slot weight residency); landing = the two
+ * landing buffers for H2D chunks; workspace = activations for max_tokens;
+ * total = the sum plus alignment.  Any output pointer may be NULL. */
+DLO_API dlo_status dlo_required_bytes(const dlo_config* cfg, size_t* slots, size_t* landing,
+                                      size_t* workspace, size_t* total);
+
+/* Validate cfg, compute every block's layout and shard size, carve the
+ * caller's arena into slots, landing buffers and workspace, create events
+ * (and streams if not given).  Allocates no device memory.  *out is owned by
+ * the library until dlo_destroy. */
+DLO_API dlo_status dlo_create(const dlo_config* cfg, dlo_ctx** out);
+
+/* Shard and pin one block: numel must equal the block's layout numel
+ * (else DLO_E_SHAPE).  Allocates dp_size pinned host shards of
+ * ceil(numel / dp_size) elements, copies the flat weight's slice into each and
+ * zero-pads the tail.  Keeps no reference to flat_bf16: the caller may free it
+ * on return.  Reloading a block replaces its shards; waits for in-flight work
+ * on the context's streams first. */
+DLO_API dlo_status dlo_load_shards(dlo_ctx* ctx, int32_t block, const uint16_t* flat_bf16,
+                                   int64_t numel);
+
+/* The streamed forward over every block, in order.  x: device fp32
+ * [tokens][d of block 0] in, [tokens][d of the last block] out, in place;
+ * its buffer must hold tokens * max_d floats.  cond: device fp32 [d_cond].
+ * Enqueues on stream (the compute stream) and the context's side streams and
+ * returns without waiting; the result is ready when stream reaches it.
+ * Errors before any enqueue: DLO_E_STATE if a block has no shards,
+ * DLO_E_INVAL if tokens is outside [1, max_tokens] or a pointer is NULL. */
+DLO_API dlo_status dlo_forward(dlo_ctx* ctx, float* x, const float* cond, int32_t tokens,
+                               hipStream_t stream);
+
+/* Synchronise the context's streams, free pinned shards, events and owned
+ * streams.  The arena returns to the caller.  NULL is a no-op. */
+DLO_API dlo_status dlo_destroy(dlo_ctx* ctx);
+
+/* The parameter table of block `block` (see dlo_block_layout). */
+DLO_API dlo_status dlo_layout(dlo_ctx* ctx, int32_t block, int64_t* numel, int64_t* shard_size,
+                              int32_t* n_params, dlo_param_desc* out, int32_t cap);
+
+/* Read-only view of pinned shard `rank` of block `block` (n = shard size). */
+DLO_API dlo_status dlo_get_shard(dlo_ctx* ctx, int32_t block, int32_t rank,
+                                 const uint16_t** ptr, int64_t* n);
+
+/* Run the real H2D -> landing -> reconstruction path for one block into
+ * slot (block % 2), synchronously, and copy the reconstructed numel elements
+ * to host_out (capacity cap elements).  Must not overlap a forward. */
+DLO_API dlo_status dlo_debug_assemble(dlo_ctx* ctx, int32_t block, uint16_t* host_out,
+                                      int64_t cap);
+
+/* Counters and the summary of the last traced forward.  Synchronises the
+ * context's streams. */
+DLO_API dlo_status dlo_get_stats(dlo_ctx* ctx, dlo_stats* out);
+
+/* The intervals of the last traced forward (cap entries at most; *n receives
+ * the number recorded).  Synchronises the context's streams. */
+DLO_API dlo_status dlo_get_trace(dlo_ctx* ctx, dlo_interval* out, int32_t cap, int32_t* n);
+
+/* Message of the last failed call on this thread ("" if none). */
+DLO_API const char* dlo_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DLO_H */

@@ -1,0 +1,81 @@
+/*
+ * dlo_ops.h -- kernel-level entry points of the streamed DiT forward.
+ *
+ * Each call launches exactly the kernel dlo_forward launches for that step,
+ * on the caller's stream, without a context.  They exist so each step can be
+ * checked against the oracle and timed on its own.  All pointers are device
+ * pointers; bf16 values are their 16-bit patterns.  Calls are asynchronous
+ * with respect to the host.  Shapes are validated on the host before any
+ * launch (DLO_E_INVAL / DLO_E_SHAPE, nothing enqueued); a failed launch
+ * returns DLO_E_HIP.  Error messages come from dlo_last_error().
+ */
+#ifndef DLO_OPS_H
+#define DLO_OPS_H
+
+#include "dlo.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Reconstruction (the single-GPU stand-in for all_gather_into_tensor,
+ * release page section "Weight sharding with AllGather reconstruction"):
+ * dst[i] = src[i] for i in [0, n).  Any 2-byte alignment is accepted; when
+ * dst and src have the same address modulo 16 bytes the kernel copies in
+ * 16-byte vectors with a scalar head and tail, which is how dlo_forward
+ * lands every chunk.  The ranges must not overlap. */
+DLO_API dlo_status dlo_op_assemble(uint16_t* dst, const uint16_t* src, int64_t n,
+                                   hipStream_t stream);
+
+/* adaLN modulation (DiT adaLN-Zero conditioning):
+ * mod[r] = sum_j w[r][j] * silu(cond[j]) + b[r] for r in [0, rows), fp32
+ * accumulation.  w: bf16 [rows][c] row-major; b: bf16 [rows]; cond, mod: fp32.
+ * c must be a multiple of 64 and at most 4096. */
+DLO_API dlo_status dlo_op_adaln(const uint16_t* w, const uint16_t* b, const float* cond,
+                                float* mod, int32_t rows, int32_t c, hipStream_t stream);
+
+/* LayerNorm (no affine, eps 1e-6, population variance) + modulation:
+ * for each token t, y = adapt(xin[t]) where xin rows have width d_in and
+ * adapt keeps the first min(d_in, d) features and zero-fills the rest;
+ * h[t][j] = bf16(LN(y)[j] * (1 + scale[j]) + shift[j]).  If xout is not NULL
+ * the adapted row y (fp32, width d) is written to xout[t] as well (the
+ * residual handed to a block of another width).  d must be a multiple of 4
+ * and at most 8192; d_in a multiple of 4. */
+DLO_API dlo_status dlo_op_ln_modulate(const float* xin, int32_t d_in, float* xout,
+                                      const float* shift, const float* scale, uint16_t* h,
+                                      int32_t tokens, int32_t d, hipStream_t stream);
+
+/* GEMM on MFMA: acc[i][j] = sum_k a[i][k] * w[j][k] (bf16 operands, fp32
+ * accumulation) for i in [0, M), j in [0, N); rows of w at or past w_rows are
+ * read as row w_rows - 1 (so padded output columns stay finite).  Epilogues:
+ *   DLO_EPI_BIAS_BF16      out bf16 [M][ldo]:  out = acc + bias[j]
+ *   DLO_EPI_BIAS_GELU_BF16 out bf16 [M][ldo]:  out = gelu_tanh(acc + bias[j])
+ *   DLO_EPI_GATED_F32      out fp32 [M][ldo]:  out += gate[j] * (acc + bias[j])
+ *   DLO_EPI_ROWBIAS_BF16   out bf16 [M][ldo]:  out = acc + bias[i]
+ * bias is bf16, gate fp32.  K must be a multiple of 64; lda, ldw multiples of
+ * 8; M, N >= 1; 1 <= w_rows <= N. */
+#define DLO_EPI_BIAS_BF16 0
+#define DLO_EPI_BIAS_GELU_BF16 1
+#define DLO_EPI_GATED_F32 2
+#define DLO_EPI_ROWBIAS_BF16 3
+DLO_API dlo_status dlo_op_gemm(int32_t epilogue, const uint16_t* a, int32_t lda, const uint16_t* w,
+                               int32_t ldw, int32_t w_rows, const uint16_t* bias, const float* gate,
+                               void* out, int32_t ldo, int32_t M, int32_t N, int32_t K,
+                               hipStream_t stream);
+
+/* Non-causal multi-head attention on MFMA with online softmax:
+ * for head h and token t, o[t][h*hd + i] = bf16(sum_s p[t][s] v[s][h*hd + i])
+ * with p = softmax_s(q[t] . k[s] / sqrt(hd)), fp32 softmax and accumulation.
+ * q[t][c] = qk[t*ld_qk + c] and k[t][c] = qk[t*ld_qk + heads*hd + c]
+ * (the q and k thirds of the QKV projection, row-major); v is given
+ * transposed: v[s][c] = vt[c*ld_vt + s], with ld_vt >= tokens rounded up to
+ * 64 and columns [tokens, ld_vt) finite.  hd = head_dim in {64, 128}. */
+DLO_API dlo_status dlo_op_attention(const uint16_t* qk, int32_t ld_qk, const uint16_t* vt,
+                                    int32_t ld_vt, uint16_t* o, int32_t ld_o, int32_t tokens,
+                                    int32_t heads, int32_t head_dim, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DLO_OPS_H */

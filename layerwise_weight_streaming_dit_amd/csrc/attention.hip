@@ -1,0 +1,237 @@
+// Non-causal multi-head attention of the DiT block on gfx950 matrix cores,
+// flash-style: the T x T scores are never materialised; each query keeps a
+// running max and sum (online softmax) while key/value tiles stream through
+// LDS.
+//
+// Orientation.  A wave owns 32 queries of one head and computes the scores
+// transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K rows are the A
+// operand (8 consecutive head-dim values per lane), the wave's Q rows the B
+// operand (kept in registers for the whole key loop).  In the 32x32 result,
+// lane l holds query (l % 32) and 16 of the 32 keys, so the softmax state of
+// a query lives in one lane pair (l, l ^ 32): row max and row sum need one
+// cross-half exchange and no LDS.
+//
+// The output is accumulated transposed too, O^T += V^T P^T: P (bf16) is the B
+// operand straight from the S^T registers, and V^T is the A operand.  In the
+// S^T layout, lane group g = l / 32 holds key offsets {8a + 4g + b} (a in
+// {0,1}, b in 0..3) of each 16-key group, so V^T is staged in LDS with the
+// keys of every 16-key group permuted by swapping bits 2 and 3 of the key
+// offset; then each lane's 8 keys are one aligned 16-byte LDS read.  V arrives
+// already transposed from the v projection (v^T = Wv h^T), so staging is
+// plain 16-byte copies split into two 8-byte LDS stores.
+//
+// Tiles: 128 queries (4 waves) per workgroup, 64 keys per step, K and V^T
+// double-buffered in LDS with XOR-swizzled 16-byte chunks; the next tile's
+// global loads are issued before the current tile's MFMAs.
+#include <math.h>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace dlo {
+
+namespace {
+
+constexpr int kAttnThreads = 256;
+constexpr int kBQ = 128;  // queries per workgroup (32 per wave)
+constexpr int kBKV = 64;  // keys per step
+
+template <int HD>
+__global__ __launch_bounds__(kAttnThreads) void attention_kernel(
+    const uint16_t* __restrict__ qk, int ld_qk, const uint16_t* __restrict__ vt, int ld_vt,
+    uint16_t* __restrict__ o, int ld_o, int T, int H, float scale_log2) {
+  constexpr int KCH = HD / 8;           // 16-byte chunks per K row
+  constexpr int KSWZ = (KCH >= 16) ? 15 : 7;
+  constexpr int NK = kBKV * KCH / kAttnThreads;  // K chunks per thread per step
+  constexpr int NV = HD * 8 / kAttnThreads;      // V^T chunks per thread per step
+  constexpr int NKK = HD / 16;                    // MFMA k-steps over the head dim
+  constexpr int NIB = HD / 32;                    // 32-row blocks of O^T
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBKV * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][HD * kBKV];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5;
+  const int h = blockIdx.y;
+  const int q0 = blockIdx.x * kBQ + wave * 32;
+  const int64_t kcol = static_cast<int64_t>(H) * HD + static_cast<int64_t>(h) * HD;
+
+  // Q fragments (B operand of S^T = K Q^T).
+  bf16x8_t qf[NKK];
+  {
+    const int qrow = min(q0 + (lane & 31), T - 1);
+    const uint16_t* qp = qk + static_cast<int64_t>(qrow) * ld_qk + static_cast<int64_t>(h) * HD + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qp + kk * 16);
+  }
+
+  // Staging addresses.
+  int k_row[NK], k_lds[NK], v_lds0[NV], v_lds1[NV];
+  const uint16_t* v_src[NV];
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const int q = tid + i * kAttnThreads, j = q / KCH, c = q % KCH;
+    k_row[i] = j;
+    k_lds[i] = j * HD + ((c ^ (j & KSWZ)) << 3);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int q = tid + i * kAttnThreads, row = q >> 3, c = q & 7;
+    v_src[i] = vt + (static_cast<int64_t>(h) * HD + row) * ld_vt + c * 8;
+    // keys 8c..8c+3 -> group position 4(c&1); keys 8c+4..8c+7 -> 8 + 4(c&1)
+    const int grp = c >> 1, half = 4 * (c & 1);
+    const int p0 = 16 * grp + half, p1 = 16 * grp + 8 + half;
+    v_lds0[i] = row * kBKV + ((((p0 >> 3) ^ (row & 7))) << 3) + (p0 & 7);
+    v_lds1[i] = row * kBKV + ((((p1 >> 3) ^ (row & 7))) << 3) + (p1 & 7);
+  }
+  const int kc = (lane & 31);
+
+  u32x4_t rk[NK], rv[NV];
+  auto load_tile = [&](int key0) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int q = tid + i * kAttnThreads, c = q % KCH;
+      const int key = min(key0 + k_row[i], T - 1);
+      rk[i] = *reinterpret_cast<const u32x4_t*>(qk + static_cast<int64_t>(key) * ld_qk + kcol + c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) rv[i] = *reinterpret_cast<const u32x4_t*>(v_src[i] + key0);
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) *reinterpret_cast<u32x4_t*>(&sK[buf][k_lds[i]]) = rk[i];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      *reinterpret_cast<u32x2_t*>(&sV[buf][v_lds0[i]]) = u32x2_t{rv[i].x, rv[i].y};
+      *reinterpret_cast<u32x2_t*>(&sV[buf][v_lds1[i]]) = u32x2_t{rv[i].z, rv[i].w};
+    }
+  };
+
+  f32x16_t oacc[NIB];
+#pragma unroll
+  for (int ib = 0; ib < NIB; ++ib)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[ib][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int ntiles = (T + kBKV - 1) / kBKV;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int cur = t & 1;
+    const bool more = t + 1 < ntiles;
+    if (more) load_tile((t + 1) * kBKV);
+
+    // ---- scores S^T for two 32-key blocks
+    f32x16_t s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      const int krow = kb * 32 + kc;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const int c = kk * 2 + g;
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sK[cur][krow * HD + ((c ^ (krow & KSWZ)) << 3)]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
+      }
+    }
+
+    // ---- online softmax (base 2; scale folded into scale_log2)
+    const int key_base = t * kBKV;
+    const bool tail = key_base + kBKV > T;
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = s[kb][r] * scale_log2;
+        if (tail) {
+          const int key = key_base + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key >= T) v = -INFINITY;
+        }
+        s[kb][r] = v;
+        mloc = fmaxf(mloc, v);
+      }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const float m_new = fmaxf(m_run, mloc);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[ib][r] *= alpha;
+
+    bf16x8_t pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        u32x4_t w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(s[kb][8 * ks + 2 * e] - m_new);
+          const float p1 = __builtin_amdgcn_exp2f(s[kb][8 * ks + 2 * e + 1] - m_new);
+          l_run += p0 + p1;
+          w[e] = pack_bf16x2(p0, p1);
+        }
+        pb[kb][ks] = __builtin_bit_cast(bf16x8_t, w);
+      }
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib) {
+      const int vrow = ib * 32 + kc;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int c = kb * 4 + ks * 2 + g;
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sV[cur][vrow * kBKV + ((c ^ (vrow & 7)) << 3)]);
+          oacc[ib] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][ks], oacc[ib], 0, 0, 0);
+        }
+    }
+
+    if (more) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and store: lane holds query q0 + l%32, head dims
+  // ib*32 + 8*rg + 4*g + 0..3 for rg = 0..3 (four consecutive -> 8 bytes).
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.0f / l_tot;
+  const int qrow = q0 + kc;
+  if (qrow < T) {
+    uint16_t* op = o + static_cast<int64_t>(qrow) * ld_o + static_cast<int64_t>(h) * HD + 4 * g;
+#pragma unroll
+    for (int ib = 0; ib < NIB; ++ib)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        u32x2_t w;
+        w.x = pack_bf16x2(oacc[ib][4 * rg] * inv, oacc[ib][4 * rg + 1] * inv);
+        w.y = pack_bf16x2(oacc[ib][4 * rg + 2] * inv, oacc[ib][4 * rg + 3] * inv);
+        *reinterpret_cast<u32x2_t*>(op + ib * 32 + 8 * rg) = w;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention(const uint16_t* qk, int ld_qk, const uint16_t* vt, int ld_vt, uint16_t* o,
+                            int ld_o, int tokens, int heads, int head_dim, hipStream_t s) {
+  if (tokens <= 0) return hipSuccess;
+  const dim3 grid((tokens + kBQ - 1) / kBQ, heads), block(kAttnThreads);
+  const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(head_dim)));
+  if (head_dim == 128)
+    hipLaunchKernelGGL(attention_kernel<128>, grid, block, 0, s, qk, ld_qk, vt, ld_vt, o, ld_o, tokens,
+                       heads, scale_log2);
+  else
+    hipLaunchKernelGGL(attention_kernel<64>, grid, block, 0, s, qk, ld_qk, vt, ld_vt, o, ld_o, tokens,
+                       heads, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace dlo

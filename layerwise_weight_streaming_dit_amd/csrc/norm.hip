@@ -1,0 +1,119 @@
+// adaLN modulation vector and LayerNorm + modulate, the two HBM-bound
+// per-token steps of the DiT block (adaLN-Zero conditioning of Peebles & Xie,
+// "Scalable Diffusion Models with Transformers", section 3.2).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace dlo {
+
+namespace {
+
+constexpr int kNormThreads = 256;
+constexpr int kMaxVec = 8;  // float4 per thread: d <= 8 * 4 * 256 = 8192
+constexpr int kAdaRowsPerWave = 4;
+
+// mod[r] = W[r] . silu(cond) + b[r].  silu(cond) is staged once per workgroup
+// in LDS; each wave walks kAdaRowsPerWave rows with 8-byte bf16 loads.
+__global__ __launch_bounds__(kNormThreads) void adaln_kernel(const uint16_t* __restrict__ w,
+                                                             const uint16_t* __restrict__ b,
+                                                             const float* __restrict__ cond,
+                                                             float* __restrict__ mod, int rows,
+                                                             int c) {
+  __shared__ float sc[4096];
+  for (int j = threadIdx.x; j < c; j += kNormThreads) sc[j] = silu(cond[j]);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r0 = (blockIdx.x * (kNormThreads / 64) + wave) * kAdaRowsPerWave;
+#pragma unroll
+  for (int rr = 0; rr < kAdaRowsPerWave; ++rr) {
+    const int r = r0 + rr;
+    if (r >= rows) break;
+    const uint16_t* wr = w + static_cast<int64_t>(r) * c;
+    float acc = 0.f;
+    for (int j = lane * 4; j < c; j += 256) {
+      const u32x2_t v = *reinterpret_cast<const u32x2_t*>(wr + j);
+      acc += __uint_as_float(v.x << 16) * sc[j] + __uint_as_float(v.x & 0xffff0000u) * sc[j + 1] +
+             __uint_as_float(v.y << 16) * sc[j + 2] + __uint_as_float(v.y & 0xffff0000u) * sc[j + 3];
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) mod[r] = acc + bf16_to_f32(b[r]);
+  }
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();  // red may still be read from a previous reduction
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < kNormThreads / 64; ++i) t += red[i];
+  return t;
+}
+
+// One workgroup per token row.  The row (adapted to width d) is held in
+// registers; mean and variance are two passes over the registers.
+__global__ __launch_bounds__(kNormThreads) void ln_modulate_kernel(
+    const float* __restrict__ xin, int d_in, float* __restrict__ xout, const float* __restrict__ shift,
+    const float* __restrict__ scale, uint16_t* __restrict__ h, int d) {
+  __shared__ float red[kNormThreads / 64];
+  const int64_t t = blockIdx.x;
+  const float* xr = xin + t * d_in;
+  const int nv = d / 4;
+  f32x4_t v[kMaxVec];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxVec; ++i) {
+    const int q = threadIdx.x + i * kNormThreads;
+    v[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (q < nv && q * 4 < d_in) v[i] = *reinterpret_cast<const f32x4_t*>(xr + q * 4);
+    s += v[i].x + v[i].y + v[i].z + v[i].w;
+  }
+  const float mean = block_sum(s, red) / static_cast<float>(d);
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxVec; ++i) {
+    const int q = threadIdx.x + i * kNormThreads;
+    if (q < nv) {
+      const f32x4_t e = v[i] - mean;
+      ss += e.x * e.x + e.y * e.y + e.z * e.z + e.w * e.w;
+    }
+  }
+  const float var = block_sum(ss, red) / static_cast<float>(d);
+  const float rstd = rsqrtf(var + 1e-6f);
+#pragma unroll
+  for (int i = 0; i < kMaxVec; ++i) {
+    const int q = threadIdx.x + i * kNormThreads;
+    if (q < nv) {
+      const f32x4_t sh = *reinterpret_cast<const f32x4_t*>(shift + q * 4);
+      const f32x4_t sc = *reinterpret_cast<const f32x4_t*>(scale + q * 4);
+      const f32x4_t y = (v[i] - mean) * rstd * (1.0f + sc) + sh;
+      u32x2_t o;
+      o.x = pack_bf16x2(y.x, y.y);
+      o.y = pack_bf16x2(y.z, y.w);
+      *reinterpret_cast<u32x2_t*>(h + t * d + q * 4) = o;
+      if (xout != nullptr) *reinterpret_cast<f32x4_t*>(xout + t * d + q * 4) = v[i];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_adaln(const uint16_t* w, const uint16_t* b, const float* cond, float* mod,
+                        int rows, int c, hipStream_t s) {
+  const int rows_per_block = (kNormThreads / 64) * kAdaRowsPerWave;
+  const int grid = (rows + rows_per_block - 1) / rows_per_block;
+  hipLaunchKernelGGL(adaln_kernel, dim3(grid), dim3(kNormThreads), 0, s, w, b, cond, mod, rows, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_ln_modulate(const float* xin, int d_in, float* xout, const float* shift,
+                              const float* scale, uint16_t* h, int tokens, int d, hipStream_t s) {
+  if (tokens <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ln_modulate_kernel, dim3(tokens), dim3(kNormThreads), 0, s, xin, d_in, xout,
+                     shift, scale, h, d);
+  return hipGetLastError();
+}
+
+}  // namespace dlo

@@ -1,0 +1,759 @@
+// Context, pinned shard store and the two-slot streaming scheduler.
+//
+// The method (vLLM-Omni "Distributed Layerwise Offload" release page):
+//  * section "Weight sharding with AllGather reconstruction" -- each block's
+//    flat weight is kept as dp equal shards of ceil(numel / dp) elements,
+//    zero-padded, in pinned host memory; the layer is rebuilt by gathering the
+//    shards in rank order;
+//  * section "Double-buffered prefetch with H2D + AllGather overlap" -- two
+//    device slots sized to the largest block, allocated once; block b+1 is
+//    copied host-to-device (copy stream) and gathered (gather stream) while
+//    block b computes from the other slot; compute waits on the gather's
+//    event; parameters are re-pointed from cached offsets;
+//  * section "DP multi-concurrency" -- invalid work is rejected before
+//    dispatch and errors fail closed.
+//
+// One GPU plays every rank here: all dp shards of a block are copied, in
+// chunks, through two landing buffers (the per-rank receive buffers), and the
+// reconstruction kernel copies each landed chunk to its place in the slot,
+// dropping the zero padding.
+//
+// Per block b (slot k = b % 2) the host enqueues, without ever blocking:
+//   copy stream   : per chunk j: wait land_free[j%2]; H2D -> landing[j%2];
+//                   record h2d_done[j%2]
+//   gather stream : wait comp_done[k] (compute of block b-2 released slot k);
+//                   per chunk j: wait h2d_done[j%2]; reconstruct into slot k;
+//                   record land_free[j%2]; finally record asm_done[k]
+//   compute stream: wait asm_done[k]; run the block from slot k;
+//                   record comp_done[k]
+// Events are re-recorded every block; each wait binds to the latest record
+// enqueued before it, which is the intended predecessor in this enqueue order.
+#include <string.h>
+
+#include <algorithm>
+#include <memory>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace dlo {
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kDefaultChunk = int64_t(1) << 24;
+constexpr int64_t kMinChunk = 4096;
+constexpr int kLandSlack = 8;  // landing offset (elements) used to co-align with the slot
+
+struct Chunk {
+  int32_t rank;
+  int64_t src_off;   // element offset inside the shard
+  int64_t len;       // elements copied host -> device
+  int64_t dst;       // element offset inside the slot (rank * S + src_off)
+  int64_t valid;     // elements reconstructed (padding dropped)
+};
+
+struct Block {
+  dlo_block_desc desc{};
+  std::vector<int64_t> extra;
+  BlockLayout layout;
+  int64_t shard = 0;  // S_b
+  std::vector<uint16_t*> shards;  // dp pinned buffers, empty until loaded
+  std::vector<Chunk> chunks;
+};
+
+struct TraceEv {
+  int kind, block, chunk, slot, landing;
+  int64_t bytes;
+  hipEvent_t start, end;
+};
+
+struct Workspace {
+  float* mod = nullptr;
+  uint16_t* h = nullptr;
+  uint16_t* qk = nullptr;
+  uint16_t* vt = nullptr;
+  uint16_t* o = nullptr;
+  uint16_t* u = nullptr;
+  float* xalt = nullptr;
+};
+
+}  // namespace
+
+}  // namespace dlo
+
+struct dlo_ctx {
+  int device = 0;
+  uint32_t flags = 0;
+  int dp = 1;
+  int max_tokens = 1;
+  int d_max = 0, m_max = 0;
+  bool mixed_width = false;
+  int64_t s_max = 0;
+  int64_t chunk_elems = 0;
+  size_t slot_bytes = 0, landing_bytes = 0, workspace_bytes = 0;
+  std::vector<dlo::Block> blocks;
+  uint16_t* slot[2] = {nullptr, nullptr};
+  uint16_t* landing[2] = {nullptr, nullptr};
+  dlo::Workspace ws;
+  hipStream_t copy_s = nullptr, gather_s = nullptr;
+  bool own_copy = false, own_gather = false;
+  hipEvent_t h2d_done[2] = {}, land_free[2] = {}, asm_done[2] = {}, comp_done[2] = {};
+  int64_t land_counter = 0;  // global chunk counter (landing buffer parity)
+  // tracing
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_next = 0;
+  std::vector<dlo::TraceEv> trace;
+  bool trace_valid = false;
+  int64_t forwards = 0;
+  bool poisoned = false;
+  bool created_events = false;
+};
+
+namespace dlo {
+
+namespace {
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+dlo_status hip_fail(dlo_ctx* ctx, hipError_t e, const char* what) {
+  if (ctx) ctx->poisoned = true;
+  return fail(DLO_E_HIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+#define DLO_HIP(ctx, call)                                   \
+  do {                                                       \
+    hipError_t _e = (call);                                  \
+    if (_e != hipSuccess) return hip_fail((ctx), _e, #call); \
+  } while (0)
+
+struct Sizes {
+  size_t slot_bytes, landing_bytes, workspace_bytes, total;
+  int64_t s_max, chunk;
+  int d_max, m_max;
+  bool mixed;
+};
+
+dlo_status validate_config(const dlo_config* cfg) {
+  if (cfg == nullptr) return fail(DLO_E_INVAL, "config is NULL");
+  if (cfg->abi_version != DLO_ABI_VERSION)
+    return fail(DLO_E_INVAL, "abi_version %d, library is %d", cfg->abi_version, DLO_ABI_VERSION);
+  if (cfg->num_blocks < 1) return fail(DLO_E_INVAL, "num_blocks %d must be >= 1", cfg->num_blocks);
+  if (cfg->blocks == nullptr) return fail(DLO_E_INVAL, "blocks is NULL");
+  if (cfg->dp_size < 1 || cfg->dp_size > 1024) return fail(DLO_E_INVAL, "dp_size %d outside [1, 1024]", cfg->dp_size);
+  if (cfg->max_tokens < 1 || cfg->max_tokens > (1 << 20))
+    return fail(DLO_E_INVAL, "max_tokens %d outside [1, 2^20]", cfg->max_tokens);
+  if (cfg->landing_chunk_elems != 0 && cfg->landing_chunk_elems < kMinChunk)
+    return fail(DLO_E_INVAL, "landing_chunk_elems %lld below %lld", (long long)cfg->landing_chunk_elems,
+                (long long)kMinChunk);
+  const int c0 = cfg->blocks[0].d_cond;
+  for (int i = 0; i < cfg->num_blocks; ++i) {
+    dlo_status st = validate_block(&cfg->blocks[i], i);
+    if (st != DLO_OK) return st;
+    if (cfg->blocks[i].d_cond != c0)
+      return fail(DLO_E_INVAL, "block %d: d_cond %d differs from block 0 (%d)", i, cfg->blocks[i].d_cond, c0);
+  }
+  return DLO_OK;
+}
+
+dlo_status compute_sizes(const dlo_config* cfg, Sizes* z) {
+  dlo_status st = validate_config(cfg);
+  if (st != DLO_OK) return st;
+  z->s_max = 0;
+  z->d_max = 0;
+  z->m_max = 0;
+  z->mixed = false;
+  for (int i = 0; i < cfg->num_blocks; ++i) {
+    BlockLayout L;
+    st = compute_layout(&cfg->blocks[i], &L);
+    if (st != DLO_OK) return st;
+    z->s_max = std::max(z->s_max, ceil_div(L.numel, cfg->dp_size));
+    z->d_max = std::max(z->d_max, cfg->blocks[i].d_model);
+    z->m_max = std::max(z->m_max, cfg->blocks[i].d_mlp);
+    if (cfg->blocks[i].d_model != cfg->blocks[0].d_model) z->mixed = true;
+  }
+  z->chunk = cfg->landing_chunk_elems ? cfg->landing_chunk_elems : std::min<int64_t>(z->s_max, kDefaultChunk);
+  z->chunk = std::min<int64_t>(z->chunk, z->s_max);
+  z->slot_bytes = align_up(size_t(2) * size_t(cfg->dp_size) * size_t(z->s_max), kAlign);
+  z->landing_bytes = 2 * align_up(size_t(2) * size_t(z->chunk + kLandSlack), kAlign);
+  const size_t T = size_t(cfg->max_tokens), Tp = align_up(T, 64);
+  const size_t d = size_t(z->d_max), m = size_t(z->m_max);
+  size_t ws = 0;
+  ws += align_up(6 * d * 4, kAlign);         // mod
+  ws += align_up(T * d * 2, kAlign);         // h
+  ws += align_up(T * 2 * d * 2, kAlign);     // qk
+  ws += align_up(d * Tp * 2, kAlign);        // vt
+  ws += align_up(T * d * 2, kAlign);         // o
+  ws += align_up(T * m * 2, kAlign);         // u
+  if (z->mixed) ws += align_up(T * d * 4, kAlign);  // xalt
+  z->workspace_bytes = ws;
+  z->total = 2 * z->slot_bytes + z->landing_bytes + z->workspace_bytes;
+  return DLO_OK;
+}
+
+void build_chunks(Block& b, int dp, int64_t chunk) {
+  b.chunks.clear();
+  const int64_t S = b.shard, n = b.layout.numel;
+  for (int r = 0; r < dp; ++r) {
+    for (int64_t off = 0; off < S; off += chunk) {
+      Chunk c;
+      c.rank = r;
+      c.src_off = off;
+      c.len = std::min(chunk, S - off);
+      c.dst = int64_t(r) * S + off;
+      c.valid = std::max<int64_t>(0, std::min(c.len, n - c.dst));
+      b.chunks.push_back(c);
+    }
+  }
+}
+
+hipEvent_t next_ev(dlo_ctx* ctx) {
+  if (ctx->ev_next >= ctx->ev_pool.size()) return nullptr;
+  return ctx->ev_pool[ctx->ev_next++];
+}
+
+// Enqueue the H2D + reconstruction of block b into slot b % 2 on the copy and
+// gather streams.  `trace` adds timed intervals.
+dlo_status enqueue_staging(dlo_ctx* ctx, int b, bool trace, hipStream_t compute_s) {
+  Block& blk = ctx->blocks[b];
+  const int k = b & 1;
+  for (size_t ci = 0; ci < blk.chunks.size(); ++ci) {
+    const Chunk& c = blk.chunks[ci];
+    const int lb = static_cast<int>(ctx->land_counter & 1);
+    ++ctx->land_counter;
+    const int64_t co = c.dst % kLandSlack;  // co-align landing with slot (mod 16 bytes)
+    uint16_t* land = ctx->landing[lb] + co;
+    // copy stream
+    DLO_HIP(ctx, hipStreamWaitEvent(ctx->copy_s, ctx->land_free[lb], 0));
+    if ((ctx->flags & DLO_FLAG_SERIALIZE) && ci == 0 && compute_s != nullptr) {
+      // synchronous schedule: nothing of block b moves before block b-1 computed
+      DLO_HIP(ctx, hipStreamWaitEvent(ctx->copy_s, ctx->comp_done[k ^ 1], 0));
+    }
+    TraceEv tv{};
+    if (trace) {
+      tv = TraceEv{DLO_IV_H2D, b, static_cast<int>(ci), -1, lb, c.len * 2, next_ev(ctx), next_ev(ctx)};
+      if (tv.start) DLO_HIP(ctx, hipEventRecord(tv.start, ctx->copy_s));
+    }
+    DLO_HIP(ctx, hipMemcpyAsync(land, blk.shards[c.rank] + c.src_off, size_t(c.len) * 2,
+                                hipMemcpyHostToDevice, ctx->copy_s));
+    if (trace && tv.end) {
+      DLO_HIP(ctx, hipEventRecord(tv.end, ctx->copy_s));
+      ctx->trace.push_back(tv);
+    }
+    DLO_HIP(ctx, hipEventRecord(ctx->h2d_done[lb], ctx->copy_s));
+    // gather stream
+    if (ci == 0) {
+      DLO_HIP(ctx, hipStreamWaitEvent(ctx->gather_s, ctx->comp_done[k], 0));
+      if (ctx->flags & DLO_FLAG_POISON_SLOTS)
+        DLO_HIP(ctx, launch_fill_nan(ctx->slot[k], ctx->slot_bytes / 2, ctx->gather_s));
+    }
+    DLO_HIP(ctx, hipStreamWaitEvent(ctx->gather_s, ctx->h2d_done[lb], 0));
+    TraceEv ta{};
+    if (trace) {
+      ta = TraceEv{DLO_IV_ASM, b, static_cast<int>(ci), k, lb, c.valid * 2, next_ev(ctx), next_ev(ctx)};
+      if (ta.start) DLO_HIP(ctx, hipEventRecord(ta.start, ctx->gather_s));
+    }
+    DLO_HIP(ctx, launch_assemble(ctx->slot[k] + c.dst, land, c.valid, ctx->gather_s));
+    if (trace && ta.end) {
+      DLO_HIP(ctx, hipEventRecord(ta.end, ctx->gather_s));
+      ctx->trace.push_back(ta);
+    }
+    DLO_HIP(ctx, hipEventRecord(ctx->land_free[lb], ctx->gather_s));
+  }
+  DLO_HIP(ctx, hipEventRecord(ctx->asm_done[k], ctx->gather_s));
+  return DLO_OK;
+}
+
+// The DiT block of `b` from slot b % 2 on the compute stream.
+dlo_status enqueue_block_compute(dlo_ctx* ctx, int b, float*& x_cur, int& d_cur, float* x_user,
+                                 const float* cond, int T, hipStream_t s) {
+  const Block& blk = ctx->blocks[b];
+  const BlockLayout& L = blk.layout;
+  const uint16_t* base = ctx->slot[b & 1];
+  // parameter re-pointing from the cached offsets
+  const uint16_t* Wqkv = base + L.off_wqkv;
+  const uint16_t* bqkv = base + L.off_bqkv;
+  const uint16_t* Wo = base + L.off_wo;
+  const uint16_t* bo = base + L.off_bo;
+  const uint16_t* W1 = base + L.off_w1;
+  const uint16_t* b1 = base + L.off_b1;
+  const uint16_t* W2 = base + L.off_w2;
+  const uint16_t* b2 = base + L.off_b2;
+  const uint16_t* Wada = base + L.off_wada;
+  const uint16_t* bada = base + L.off_bada;
+  const int d = blk.desc.d_model, m = blk.desc.d_mlp, H = blk.desc.n_heads, c = blk.desc.d_cond;
+  const int hd = d / H;
+  const int Tp = static_cast<int>(align_up(size_t(T), 64));
+  const Workspace& w = ctx->ws;
+  float* mod = w.mod;
+
+  DLO_HIP(ctx, launch_adaln(Wada, bada, cond, mod, 6 * d, c, s));
+  if (d != d_cur) {
+    float* x_new = (x_cur == x_user) ? w.xalt : x_user;
+    DLO_HIP(ctx, launch_ln_modulate(x_cur, d_cur, x_new, mod, mod + d, w.h, T, d, s));
+    x_cur = x_new;
+    d_cur = d;
+  } else {
+    DLO_HIP(ctx, launch_ln_modulate(x_cur, d, nullptr, mod, mod + d, w.h, T, d, s));
+  }
+  GemmArgs g{};
+  // q, k projection: qk[T][2d] = h Wqk^T + bqk
+  g = GemmArgs{w.h, Wqkv, bqkv, nullptr, w.qk, d, d, 2 * d, T, 2 * d, d, 2 * d};
+  DLO_HIP(ctx, launch_gemm(EPI_BIAS_BF16, g, s));
+  // v projection, transposed: vt[d][Tp] = Wv h^T + bv (columns >= T finite)
+  g = GemmArgs{Wqkv + int64_t(2) * d * d, w.h, bqkv + 2 * d, nullptr, w.vt, d, d, Tp, d, Tp, d, T};
+  DLO_HIP(ctx, launch_gemm(EPI_ROWBIAS_BF16, g, s));
+  DLO_HIP(ctx, launch_attention(w.qk, 2 * d, w.vt, Tp, w.o, d, T, H, hd, s));
+  // x += gate1 * (o Wo^T + bo)
+  g = GemmArgs{w.o, Wo, bo, mod + 2 * d, x_cur, d, d, d, T, d, d, d};
+  DLO_HIP(ctx, launch_gemm(EPI_GATED_F32, g, s));
+  DLO_HIP(ctx, launch_ln_modulate(x_cur, d, nullptr, mod + 3 * d, mod + 4 * d, w.h, T, d, s));
+  // u = gelu(h2 W1^T + b1)
+  g = GemmArgs{w.h, W1, b1, nullptr, w.u, d, d, m, T, m, d, m};
+  DLO_HIP(ctx, launch_gemm(EPI_BIAS_GELU_BF16, g, s));
+  // x += gate2 * (u W2^T + b2)
+  g = GemmArgs{w.u, W2, b2, mod + 5 * d, x_cur, m, m, d, T, d, m, d};
+  DLO_HIP(ctx, launch_gemm(EPI_GATED_F32, g, s));
+  return DLO_OK;
+}
+
+dlo_status check_ctx(dlo_ctx* ctx) {
+  if (ctx == nullptr) return fail(DLO_E_INVAL, "context is NULL");
+  if (ctx->poisoned) return fail(DLO_E_POISONED, "context poisoned by an earlier HIP error");
+  return DLO_OK;
+}
+
+dlo_status sync_ctx(dlo_ctx* ctx) {
+  DLO_HIP(ctx, hipStreamSynchronize(ctx->copy_s));
+  DLO_HIP(ctx, hipStreamSynchronize(ctx->gather_s));
+  DLO_HIP(ctx, hipEventSynchronize(ctx->comp_done[0]));
+  DLO_HIP(ctx, hipEventSynchronize(ctx->comp_done[1]));
+  return DLO_OK;
+}
+
+void free_ctx(dlo_ctx* ctx) {
+  for (auto& b : ctx->blocks)
+    for (auto* p : b.shards)
+      if (p) (void)hipHostFree(p);
+  for (auto e : ctx->ev_pool) (void)hipEventDestroy(e);
+  if (ctx->created_events) {
+    for (int i = 0; i < 2; ++i) {
+      (void)hipEventDestroy(ctx->h2d_done[i]);
+      (void)hipEventDestroy(ctx->land_free[i]);
+      (void)hipEventDestroy(ctx->asm_done[i]);
+      (void)hipEventDestroy(ctx->comp_done[i]);
+    }
+  }
+  if (ctx->own_copy && ctx->copy_s) (void)hipStreamDestroy(ctx->copy_s);
+  if (ctx->own_gather && ctx->gather_s) (void)hipStreamDestroy(ctx->gather_s);
+  delete ctx;
+}
+
+}  // namespace
+
+}  // namespace dlo
+
+using namespace dlo;
+
+extern "C" DLO_API dlo_status dlo_required_bytes(const dlo_config* cfg, size_t* slots, size_t* landing,
+                                                 size_t* workspace, size_t* total) {
+  clear_error();
+  Sizes z;
+  dlo_status st = compute_sizes(cfg, &z);
+  if (st != DLO_OK) return st;
+  if (slots) *slots = 2 * z.slot_bytes;
+  if (landing) *landing = z.landing_bytes;
+  if (workspace) *workspace = z.workspace_bytes;
+  if (total) *total = z.total;
+  return DLO_OK;
+}
+
+extern "C" DLO_API dlo_status dlo_create(const dlo_config* cfg, dlo_ctx** out) {
+  clear_error();
+  if (out == nullptr) return fail(DLO_E_INVAL, "out is NULL");
+  *out = nullptr;
+  Sizes z;
+  dlo_status st = compute_sizes(cfg, &z);
+  if (st != DLO_OK) return st;
+  if (cfg->arena == nullptr) return fail(DLO_E_INVAL, "arena is NULL");
+  if (reinterpret_cast<uintptr_t>(cfg->arena) % kAlign != 0) return fail(DLO_E_INVAL, "arena not 256-byte aligned");
+  if (cfg->arena_bytes < z.total)
+    return fail(DLO_E_DEV_OOM, "arena holds %zu bytes, %zu required", cfg->arena_bytes, z.total);
+
+  std::unique_ptr<dlo_ctx, void (*)(dlo_ctx*)> ctx(new dlo_ctx(), free_ctx);
+  ctx->device = cfg->device;
+  ctx->flags = cfg->flags;
+  ctx->dp = cfg->dp_size;
+  ctx->max_tokens = cfg->max_tokens;
+  ctx->d_max = z.d_max;
+  ctx->m_max = z.m_max;
+  ctx->mixed_width = z.mixed;
+  ctx->s_max = z.s_max;
+  ctx->chunk_elems = z.chunk;
+  ctx->slot_bytes = z.slot_bytes;
+  ctx->landing_bytes = z.landing_bytes;
+  ctx->workspace_bytes = z.workspace_bytes;
+  ctx->blocks.resize(cfg->num_blocks);
+  for (int i = 0; i < cfg->num_blocks; ++i) {
+    Block& b = ctx->blocks[i];
+    b.desc = cfg->blocks[i];
+    b.extra.assign(cfg->blocks[i].extra_len, cfg->blocks[i].extra_len + cfg->blocks[i].n_extra);
+    b.desc.extra_len = b.extra.empty() ? nullptr : b.extra.data();
+    st = compute_layout(&b.desc, &b.layout);
+    if (st != DLO_OK) return st;
+    b.shard = ceil_div(b.layout.numel, ctx->dp);
+    build_chunks(b, ctx->dp, ctx->chunk_elems);
+  }
+  // carve the arena: slot 0, slot 1, landing 0, landing 1, workspace
+  char* p = static_cast<char*>(cfg->arena);
+  ctx->slot[0] = reinterpret_cast<uint16_t*>(p);
+  p += z.slot_bytes;
+  ctx->slot[1] = reinterpret_cast<uint16_t*>(p);
+  p += z.slot_bytes;
+  const size_t land_one = z.landing_bytes / 2;
+  ctx->landing[0] = reinterpret_cast<uint16_t*>(p);
+  p += land_one;
+  ctx->landing[1] = reinterpret_cast<uint16_t*>(p);
+  p += land_one;
+  const size_t T = size_t(cfg->max_tokens), Tp = align_up(T, 64), d = size_t(z.d_max), m = size_t(z.m_max);
+  auto take = [&](size_t bytes) {
+    char* r = p;
+    p += align_up(bytes, kAlign);
+    return r;
+  };
+  ctx->ws.mod = reinterpret_cast<float*>(take(6 * d * 4));
+  ctx->ws.h = reinterpret_cast<uint16_t*>(take(T * d * 2));
+  ctx->ws.qk = reinterpret_cast<uint16_t*>(take(T * 2 * d * 2));
+  ctx->ws.vt = reinterpret_cast<uint16_t*>(take(d * Tp * 2));
+  ctx->ws.o = reinterpret_cast<uint16_t*>(take(T * d * 2));
+  ctx->ws.u = reinterpret_cast<uint16_t*>(take(T * m * 2));
+  if (z.mixed) ctx->ws.xalt = reinterpret_cast<float*>(take(T * d * 4));
+
+  DeviceGuard dg(ctx->device);
+  if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
+  dlo_ctx* c = ctx.get();
+  if (cfg->copy_stream) {
+    c->copy_s = cfg->copy_stream;
+  } else {
+    DLO_HIP(nullptr, hipStreamCreateWithFlags(&c->copy_s, hipStreamNonBlocking));
+    c->own_copy = true;
+  }
+  if (cfg->gather_stream) {
+    c->gather_s = cfg->gather_stream;
+  } else {
+    DLO_HIP(nullptr, hipStreamCreateWithFlags(&c->gather_s, hipStreamNonBlocking));
+    c->own_gather = true;
+  }
+  for (int i = 0; i < 2; ++i) {
+    DLO_HIP(nullptr, hipEventCreateWithFlags(&c->h2d_done[i], hipEventDisableTiming));
+    DLO_HIP(nullptr, hipEventCreateWithFlags(&c->land_free[i], hipEventDisableTiming));
+    DLO_HIP(nullptr, hipEventCreateWithFlags(&c->asm_done[i], hipEventDisableTiming));
+    DLO_HIP(nullptr, hipEventCreateWithFlags(&c->comp_done[i], hipEventDisableTiming));
+    c->created_events = true;
+  }
+  // initial records so the first waits are satisfied
+  for (int i = 0; i < 2; ++i) {
+    DLO_HIP(nullptr, hipEventRecord(c->land_free[i], c->gather_s));
+    DLO_HIP(nullptr, hipEventRecord(c->comp_done[i], c->gather_s));
+  }
+  if (c->flags & DLO_FLAG_TRACE) {
+    size_t n = 0;
+    for (auto& b : c->blocks) n += 4 * b.chunks.size() + 2;
+    c->ev_pool.resize(n, nullptr);
+    for (size_t i = 0; i < n; ++i) DLO_HIP(nullptr, hipEventCreate(&c->ev_pool[i]));
+  }
+  DLO_HIP(nullptr, hipStreamSynchronize(c->gather_s));
+  *out = ctx.release();
+  return DLO_OK;
+}
+
+extern "C" DLO_API dlo_status dlo_load_shards(dlo_ctx* ctx, int32_t block, const uint16_t* flat, int64_t numel) {
+  clear_error();
+  dlo_status st = check_ctx(ctx);
+  if (st != DLO_OK) return st;
+  if (block < 0 || block >= static_cast<int>(ctx->blocks.size()))
+    return fail(DLO_E_INVAL, "block %d outside [0, %zu)", block, ctx->blocks.size());
+  Block& b = ctx->blocks[block];
+  if (numel != b.layout.numel)
+    return fail(DLO_E_SHAPE, "block %d: numel %lld, layout has %lld", block, (long long)numel,
+                (long long)b.layout.numel);
+  if (flat == nullptr) return fail(DLO_E_INVAL, "flat weight is NULL");
+  DeviceGuard dg(ctx->device);
+  if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
+  // no in-flight copy may read the shards being replaced
+  DLO_HIP(ctx, hipStreamSynchronize(ctx->copy_s));
+  const int64_t S = b.shard;
+  if (b.shards.empty()) {
+    b.shards.assign(ctx->dp, nullptr);
+    for (int r = 0; r < ctx->dp; ++r) {
+      void* p = nullptr;
+      hipError_t e = hipHostMalloc(&p, size_t(std::max<int64_t>(S, 1)) * 2, hipHostMallocDefault);
+      if (e != hipSuccess || p == nullptr) {
+        for (auto*& q : b.shards)
+          if (q) {
+            (void)hipHostFree(q);
+            q = nullptr;
+          }
+        b.shards.clear();
+        (void)hipGetLastError();
+        return fail(DLO_E_HOST_OOM, "block %d: pinned allocation of %lld bytes failed", block,
+                    (long long)(S * 2));
+      }
+      b.shards[r] = static_cast<uint16_t*>(p);
+    }
+  }
+  for (int r = 0; r < ctx->dp; ++r) {
+    const int64_t lo = int64_t(r) * S;
+    const int64_t n = std::max<int64_t>(0, std::min(S, numel - lo));
+    if (n > 0) memcpy(b.shards[r], flat + lo, size_t(n) * 2);
+    if (n < S) memset(b.shards[r] + n, 0, size_t(S - n) * 2);
+  }
+  return DLO_OK;
+}
+
+extern "C" DLO_API dlo_status dlo_forward(dlo_ctx* ctx, float* x, const float* cond, int32_t tokens,
+                                          hipStream_t stream) {
+  clear_error();
+  dlo_status st = check_ctx(ctx);
+  if (st != DLO_OK) return st;
+  if (x == nullptr || cond == nullptr) return fail(DLO_E_INVAL, "x or cond is NULL");
+  if (tokens < 1 || tokens > ctx->max_tokens)
+    return fail(DLO_E_INVAL, "tokens %d outside [1, %d]", tokens, ctx->max_tokens);
+  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(cond) % 16)
+    return fail(DLO_E_INVAL, "x and cond must be 16-byte aligned");
+  for (size_t i = 0; i < ctx->blocks.size(); ++i)
+    if (ctx->blocks[i].shards.empty()) return fail(DLO_E_STATE, "block %zu has no shards loaded", i);
+  DeviceGuard dg(ctx->device);
+  if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
+
+  const bool trace = (ctx->flags & DLO_FLAG_TRACE) != 0;
+  if (trace) {
+    ctx->trace.clear();
+    ctx->ev_next = 0;
+    ctx->trace_valid = false;
+  }
+  float* x_cur = x;
+  int d_cur = ctx->blocks[0].desc.d_model;
+  const int L = static_cast<int>(ctx->blocks.size());
+  for (int b = 0; b < L; ++b) {
+    st = enqueue_staging(ctx, b, trace, stream);
+    if (st != DLO_OK) return st;
+    const int k = b & 1;
+    DLO_HIP(ctx, hipStreamWaitEvent(stream, ctx->asm_done[k], 0));
+    TraceEv tc{};
+    if (trace) {
+      tc = TraceEv{DLO_IV_COMPUTE, b, -1, k, -1, 0, next_ev(ctx), next_ev(ctx)};
+      if (tc.start) DLO_HIP(ctx, hipEventRecord(tc.start, stream));
+    }
+    st = enqueue_block_compute(ctx, b, x_cur, d_cur, x, cond, tokens, stream);
+    if (st != DLO_OK) return st;
+    if (trace && tc.end) {
+      DLO_HIP(ctx, hipEventRecord(tc.end, stream));
+      ctx->trace.push_back(tc);
+    }
+    DLO_HIP(ctx, hipEventRecord(ctx->comp_done[k], stream));
+  }
+  if (x_cur != x)
+    DLO_HIP(ctx, hipMemcpyAsync(x, x_cur, size_t(tokens) * size_t(d_cur) * 4, hipMemcpyDeviceToDevice, stream));
+  if (trace) ctx->trace_valid = true;
+  ++ctx->forwards;
+  return DLO_OK;
+}
+
+extern "C" DLO_API dlo_status dlo_destroy(dlo_ctx* ctx) {
+  clear_error();
+  if (ctx == nullptr) return DLO_OK;
+  {
+    DeviceGuard dg(ctx->device);
+    if (!ctx->poisoned) {
+      (void)hipStreamSynchronize(ctx->copy_s);
+      (void)hipStreamSynchronize(ctx->gather_s);
+      (void)hipEventSynchronize(ctx->comp_done[0]);
+      (void)hipEventSynchronize(ctx->comp_done[1]);
+    }
+  }
+  free_ctx(ctx);
+  return DLO_OK;
+}
+
+extern "C" DLO_API dlo_status dlo_layout(dlo_ctx* ctx, int32_t block, int64_t* numel, int64_t* shard_size,
+                                         int32_t* n_params, dlo_param_desc* out, int32_t cap) {
+  clear_error();
+  if (ctx == nullptr) return fail(DLO_E_INVAL, "context is NULL");
+  if (block < 0 || block >= static_cast<int>(ctx->blocks.size()))
+    return fail(DLO_E_INVAL, "block %d outside [0, %zu)", block, ctx->blocks.size());
+  const Block& b = ctx->blocks[block];
+  if (numel) *numel = b.layout.numel;
+  if (shard_size) *shard_size = b.shard;
+  if (n_params) *n_params = b.layout.n_params;
+  if (out) {
+    if (cap < b.layout.n_params) return fail(DLO_E_INVAL, "cap %d < %d parameters", cap, b.layout.n_params);
+    memcpy(out, b.layout.params, sizeof(dlo_param_desc) * b.layout.n_params);
+  }
+  return DLO_OK;
+}
+
+extern "C" DLO_API dlo_status dlo_get_shard(dlo_ctx* ctx, int32_t block, int32_t rank, const uint16_t** ptr,
+                                            int64_t* n) {
+  clear_error();
+  if (ctx == nullptr || ptr == nullptr || n == nullptr) return fail(DLO_E_INVAL, "NULL argument");
+  if (block < 0 || block >= static_cast<int>(ctx->blocks.size()))
+    return fail(DLO_E_INVAL, "block %d outside [0, %zu)", block, ctx->blocks.size());
+  if (rank < 0 || rank >= ctx->dp) return fail(DLO_E_INVAL, "rank %d outside [0, %d)", rank, ctx->dp);
+  const Block& b = ctx->blocks[block];
+  if (b.shards.empty()) return fail(DLO_E_STATE, "block %d has no shards loaded", block);
+  *ptr = b.shards[rank];
+  *n = b.shard;
+  return DLO_OK;
+}
+
+extern "C" DLO_API dlo_status dlo_debug_assemble(dlo_ctx* ctx, int32_t block, uint16_t* host_out, int64_t cap) {
+  clear_error();
+  dlo_status st = check_ctx(ctx);
+  if (st != DLO_OK) return st;
+  if (block < 0 || block >= static_cast<int>(ctx->blocks.size()))
+    return fail(DLO_E_INVAL, "block %d outside [0, %zu)", block, ctx->blocks.size());
+  Block& b = ctx->blocks[block];
+  if (b.shards.empty()) return fail(DLO_E_STATE, "block %d has no shards loaded", block);
+  if (host_out == nullptr || cap < b.layout.numel)
+    return fail(DLO_E_INVAL, "host_out must hold %lld elements", (long long)b.layout.numel);
+  DeviceGuard dg(ctx->device);
+  if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
+  st = enqueue_staging(ctx, block, false, nullptr);
+  if (st != DLO_OK) return st;
+  DLO_HIP(ctx, hipStreamSynchronize(ctx->gather_s));
+  DLO_HIP(ctx, hipMemcpy(host_out, ctx->slot[block & 1], size_t(b.layout.numel) * 2, hipMemcpyDeviceToHost));
+  return DLO_OK;
+}
+
+namespace {
+
+dlo_status collect_trace(dlo_ctx* ctx, std::vector<dlo_interval>& out, dlo_stats* s) {
+  out.clear();
+  if (!ctx->trace_valid) return DLO_OK;
+  dlo_status st = sync_ctx(ctx);
+  if (st != DLO_OK) return st;
+  hipEvent_t base = nullptr;
+  float best = 0.f;
+  // base = earliest start event
+  for (auto& t : ctx->trace) {
+    if (!t.start) continue;
+    if (!base) {
+      base = t.start;
+      continue;
+    }
+    float ms = 0.f;
+    DLO_HIP(ctx, hipEventElapsedTime(&ms, base, t.start));
+    if (ms < best) {
+      best = ms;
+    }
+  }
+  if (!base) return DLO_OK;
+  double t_end = 0.0;
+  for (auto& t : ctx->trace) {
+    float a = 0.f, e = 0.f;
+    DLO_HIP(ctx, hipEventElapsedTime(&a, base, t.start));
+    DLO_HIP(ctx, hipEventElapsedTime(&e, base, t.end));
+    dlo_interval iv{};
+    iv.kind = t.kind;
+    iv.block = t.block;
+    iv.chunk = t.chunk;
+    iv.slot = t.slot;
+    iv.landing = t.landing;
+    iv.bytes = t.bytes;
+    iv.start_ms = double(a) - double(best);
+    iv.end_ms = double(e) - double(best);
+    t_end = std::max(t_end, iv.end_ms);
+    out.push_back(iv);
+  }
+  if (s) {
+    s->last_forward_ms = t_end;
+    double h = 0, a = 0, c = 0;
+    for (auto& iv : out) {
+      const double dur = iv.end_ms - iv.start_ms;
+      if (iv.kind == DLO_IV_H2D) h += dur;
+      if (iv.kind == DLO_IV_ASM) a += dur;
+      if (iv.kind == DLO_IV_COMPUTE) c += dur;
+    }
+    s->sum_h2d_ms = h;
+    s->sum_asm_ms = a;
+    s->sum_compute_ms = c;
+    // residency: block b occupies its slot from its first reconstruction
+    // start to its compute end
+    const int L = static_cast<int>(ctx->blocks.size());
+    std::vector<double> first(L, 1e300), last(L, -1e300);
+    for (auto& iv : out) {
+      if (iv.kind == DLO_IV_ASM) first[iv.block] = std::min(first[iv.block], iv.start_ms);
+      if (iv.kind == DLO_IV_COMPUTE) last[iv.block] = std::max(last[iv.block], iv.end_ms);
+    }
+    std::vector<std::pair<double, int>> evs;
+    for (int b2 = 0; b2 < L; ++b2) {
+      evs.push_back({first[b2], 1});
+      evs.push_back({last[b2], -1});
+    }
+    std::sort(evs.begin(), evs.end(), [](auto& u, auto& v) {
+      return u.first < v.first || (u.first == v.first && u.second < v.second);
+    });
+    int cur = 0, hw = 0;
+    for (auto& e2 : evs) {
+      cur += e2.second;
+      hw = std::max(hw, cur);
+    }
+    s->residency_high_water = hw;
+    s->n_intervals = static_cast<int32_t>(out.size());
+  }
+  return DLO_OK;
+}
+
+}  // namespace
+
+extern "C" DLO_API dlo_status dlo_get_stats(dlo_ctx* ctx, dlo_stats* out) {
+  clear_error();
+  dlo_status st = check_ctx(ctx);
+  if (st != DLO_OK) return st;
+  if (out == nullptr) return fail(DLO_E_INVAL, "out is NULL");
+  DeviceGuard dg(ctx->device);
+  memset(out, 0, sizeof(*out));
+  out->num_blocks = static_cast<int32_t>(ctx->blocks.size());
+  out->dp_size = ctx->dp;
+  out->forwards = ctx->forwards;
+  out->max_shard_elems = ctx->s_max;
+  out->slot_bytes = ctx->slot_bytes;
+  out->landing_bytes = ctx->landing_bytes;
+  out->workspace_bytes = ctx->workspace_bytes;
+  int64_t hb = 0;
+  for (auto& b : ctx->blocks) hb += int64_t(2) * ctx->dp * b.shard;
+  out->h2d_bytes_per_forward = hb;
+  std::vector<dlo_interval> tmp;
+  return collect_trace(ctx, tmp, out);
+}
+
+extern "C" DLO_API dlo_status dlo_get_trace(dlo_ctx* ctx, dlo_interval* out, int32_t cap, int32_t* n) {
+  clear_error();
+  dlo_status st = check_ctx(ctx);
+  if (st != DLO_OK) return st;
+  if (n == nullptr) return fail(DLO_E_INVAL, "n is NULL");
+  DeviceGuard dg(ctx->device);
+  std::vector<dlo_interval> tmp;
+  st = collect_trace(ctx, tmp, nullptr);
+  if (st != DLO_OK) return st;
+  *n = static_cast<int32_t>(tmp.size());
+  if (out) {
+    if (cap < *n) return fail(DLO_E_INVAL, "cap %d < %d intervals", cap, *n);
+    memcpy(out, tmp.data(), sizeof(dlo_interval) * tmp.size());
+  }
+  return DLO_OK;
+}

@@ -1,0 +1,40 @@
+"""Helpers for the GPU tests (device copies, the contract tolerance)."""
+import numpy as np
+
+RTOL = 2e-2
+ATOL = 2e-2
+
+
+def torch():
+    import torch as _t
+    return _t
+
+
+def dev(a: np.ndarray):
+    """Copy a numpy array to cuda:0 with the same bytes (uint16 -> int16)."""
+    t = torch()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return t.from_numpy(a).cuda()
+
+
+def host(t, dtype=None) -> np.ndarray:
+    a = t.detach().cpu().numpy()
+    if dtype is not None:
+        a = a.view(dtype)
+    return a
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def within(got, want, rtol=RTOL, atol=ATOL):
+    """|got - want| <= atol + rtol * |want| everywhere; returns (ok, max_abs, max_rel)."""
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    err = np.abs(got - want)
+    ok = bool(np.all(err <= atol + rtol * np.abs(want))) and bool(np.all(np.isfinite(got)))
+    rel = err / np.maximum(np.abs(want), 1e-30)
+    return ok, float(err.max(initial=0.0)), float(rel.max(initial=0.0))

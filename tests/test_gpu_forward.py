@@ -1,0 +1,261 @@
+"""The streamed forward through the C ABI against the oracle, plus the
+invariants the method fixes: bit-exact reconstruction, exact adaLN-Zero
+identity, outputs independent of dp_size / schedule / chunking, the
+two-slot schedule, and fail-closed errors."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import dit as D, layout as OL, shard as OS, trace as OT
+from gpu_util import dev, host, within, torch
+
+pytestmark = pytest.mark.gpu
+
+import layerwise_weight_streaming_dit_amd as dlo
+
+
+def _weights(wl, blocks=None):
+    blocks = range(wl.num_blocks) if blocks is None else blocks
+    return {b: synth.block_weights(wl.wid, b, OL.block_numel(wl.blocks[b])) for b in blocks}
+
+
+def _ctx(shapes, dp, T, flags=0, chunk=0):
+    return dlo.StreamedDiT(shapes, dp, T, flags=flags, chunk_elems=chunk)
+
+
+def _run(ctx, x, cond):
+    t = torch()
+    T, d0 = x.shape
+    xbuf = t.zeros(T * ctx.max_d, dtype=t.float32, device="cuda")
+    xbuf[: T * d0] = dev(x.reshape(-1))
+    out = ctx.forward(xbuf, dev(cond), T)
+    t.cuda.synchronize()
+    return host(out).copy()
+
+
+# ------------------------------------------------------------ reconstruction
+
+def test_debug_assemble_tiny_bit_exact():
+    wl = synth.workload("tiny")
+    W = _weights(wl)
+    ctx = _ctx(list(wl.blocks), 4, wl.tokens)
+    for b, flat in W.items():
+        ctx.load_shards(b, flat)
+        ref = OS.shard(flat, 4)
+        for r in range(4):
+            assert np.array_equal(ctx.get_shard(b, r), ref[r])
+    for b, flat in W.items():
+        got = ctx.debug_assemble(b)
+        assert np.array_equal(got, OS.unshard(OS.shard(flat, 4), len(flat)))
+
+
+@pytest.mark.parametrize("dp", [3, 8])
+def test_debug_assemble_irregular_bit_exact(dp):
+    wl = synth.workload("irregular")
+    shapes = list(wl.blocks[:2])
+    ctx = _ctx(shapes, dp, 64)
+    for b in range(2):
+        flat = synth.block_weights(wl.wid, b, OL.block_numel(shapes[b]))
+        ctx.load_shards(b, flat)
+        assert np.array_equal(ctx.debug_assemble(b), flat)
+
+
+def test_debug_assemble_random_numel_sweep():
+    rng = np.random.default_rng(2024)
+    for it in range(12):
+        dp = int(rng.integers(1, 17))
+        extra = tuple(int(v) for v in rng.integers(0, 5000, size=int(rng.integers(1, 6))))
+        shp = synth.BlockShape(128, 2, 128, 64, extra)
+        n = OL.block_numel(shp)
+        chunk = int(rng.choice([4096, 5000, 1 << 20]))
+        ctx = _ctx([shp], dp, 16, chunk=chunk)
+        flat = rng.integers(0, 1 << 16, size=n, dtype=np.uint16)
+        ctx.load_shards(0, flat)
+        assert np.array_equal(ctx.debug_assemble(0), flat), (dp, extra, chunk)
+        ctx.close()
+
+
+# ---------------------------------------------------------- forward parity
+
+def test_tiny_forward_matches_oracle():
+    wl = synth.workload("tiny")
+    W = _weights(wl)
+    x = synth.activations(wl.tokens, 256)
+    cond = synth.conditioning(256)
+    ctx = _ctx(list(wl.blocks), 4, wl.tokens)
+    for b, flat in W.items():
+        ctx.load_shards(b, flat)
+    got = _run(ctx, x, cond)
+    want = D.dit_forward([W[b] for b in range(wl.num_blocks)], wl.blocks, x, cond)
+    ok, ma, mr = within(got, want)
+    print(f"tiny chained: max_abs {ma:.3e} max_rel {mr:.3e}")
+    assert ok, (ma, mr)
+
+
+def test_tiny_per_block_matches_oracle():
+    wl = synth.workload("tiny")
+    W = _weights(wl)
+    x = synth.activations(wl.tokens, 256)
+    cond = synth.conditioning(256)
+    xin = x.astype(np.float64)
+    for b in range(wl.num_blocks):
+        ctx = _ctx([wl.blocks[b]], 4, wl.tokens)
+        ctx.load_shards(0, W[b])
+        got = _run(ctx, xin.astype(np.float32), cond)
+        want = D.dit_block(W[b], wl.blocks[b], xin.astype(np.float32), cond)
+        ok, ma, mr = within(got, want)
+        assert ok, (b, ma, mr)
+        xin = want
+        ctx.close()
+
+
+@pytest.mark.parametrize("T", [1, 5, 100, 257])
+def test_tiny_ragged_tokens(T):
+    wl = synth.workload("tiny")
+    W = _weights(wl, [0, 1])
+    shapes = list(wl.blocks[:2])
+    x = synth.activations(T, 256)
+    cond = synth.conditioning(256)
+    ctx = _ctx(shapes, 4, 512)
+    for b in range(2):
+        ctx.load_shards(b, W[b])
+    got = _run(ctx, x, cond)
+    want = D.dit_forward([W[0], W[1]], shapes, x, cond)
+    ok, ma, mr = within(got, want)
+    assert ok, (T, ma, mr)
+
+
+def _sampled_block_check(wl, b, T, dp, rows=48):
+    shp = wl.blocks[b]
+    flat = synth.block_weights(wl.wid, b, OL.block_numel(shp))
+    x = synth.activations(T, shp.d_model)
+    cond = synth.conditioning(shp.d_cond)
+    ctx = _ctx([shp], dp, T)
+    ctx.load_shards(0, flat)
+    got = _run(ctx, x, cond)
+    ctx.close()
+    idx = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(b).integers(0, T, size=rows)]))
+    want = D.dit_block(flat, shp, x, cond, rows=idx)
+    ok, ma, mr = within(got[idx], want)
+    print(f"{wl.name} block {b} T={T}: max_abs {ma:.3e} max_rel {mr:.3e}")
+    assert ok, (ma, mr)
+
+
+@pytest.mark.parametrize("b", [0, 27])
+def test_image_block_full_size_sampled_rows(b):
+    wl = synth.workload("image")
+    _sampled_block_check(wl, b, wl.tokens, 4)
+
+
+# --------------------------------------------------------------- invariants
+
+def _tiny_out(dp=4, flags=0, chunk=0, W=None, x=None):
+    wl = synth.workload("tiny")
+    W = W or _weights(wl)
+    x = synth.activations(wl.tokens, 256) if x is None else x
+    ctx = _ctx(list(wl.blocks), dp, wl.tokens, flags=flags, chunk=chunk)
+    for b, flat in W.items():
+        ctx.load_shards(b, flat)
+    out = _run(ctx, x, synth.conditioning(256))
+    return out, ctx
+
+
+def test_outputs_identical_across_dp_chunking_and_schedule():
+    base, _ = _tiny_out()
+    for dp in (1, 3, 8):
+        assert np.array_equal(_tiny_out(dp=dp)[0], base), dp
+    assert np.array_equal(_tiny_out(chunk=4096)[0], base)
+    assert np.array_equal(_tiny_out(flags=dlo.FLAG_SERIALIZE)[0], base)
+    assert np.array_equal(_tiny_out(flags=dlo.FLAG_POISON_SLOTS)[0], base)
+
+
+def test_chained_equals_successive_single_block_forwards():
+    wl = synth.workload("tiny")
+    W = _weights(wl)
+    base, _ = _tiny_out(W=W)
+    x = synth.activations(wl.tokens, 256)
+    for b in range(wl.num_blocks):
+        ctx = _ctx([wl.blocks[b]], 4, wl.tokens)
+        ctx.load_shards(0, W[b])
+        x = _run(ctx, x, synth.conditioning(256))
+        ctx.close()
+    assert np.array_equal(x, base)
+
+
+def test_adaln_zero_identity_exact():
+    wl = synth.workload("tiny")
+    W = _weights(wl)
+    for b, flat in W.items():
+        tab = {p.name: p for p in OL.param_table(wl.blocks[b])}
+        d = wl.blocks[b].d_model
+        c = wl.blocks[b].d_cond
+        flat = flat.copy()
+        wada = flat[tab["Wada"].offset:tab["Wada"].offset + tab["Wada"].numel].reshape(6 * d, c)
+        wada[2 * d:3 * d] = 0
+        wada[5 * d:6 * d] = 0
+        bada = flat[tab["bada"].offset:tab["bada"].offset + tab["bada"].numel]
+        bada[2 * d:3 * d] = 0
+        bada[5 * d:6 * d] = 0
+        W[b] = flat
+    x = synth.activations(wl.tokens, 256)
+    out, _ = _tiny_out(W=W, x=x)
+    assert np.array_equal(out, x)
+
+
+def test_repeated_forwards_identical_and_allocate_nothing():
+    t = torch()
+    wl = synth.workload("tiny")
+    W = _weights(wl)
+    ctx = _ctx(list(wl.blocks), 4, wl.tokens)
+    for b, flat in W.items():
+        ctx.load_shards(b, flat)
+    x = synth.activations(wl.tokens, 256)
+    first = _run(ctx, x, synth.conditioning(256))
+    t.cuda.synchronize()
+    free0 = t.cuda.mem_get_info()[0]
+    for _ in range(3):
+        assert np.array_equal(_run(ctx, x, synth.conditioning(256)), first)
+    t.cuda.synchronize()
+    assert t.cuda.mem_get_info()[0] == free0
+
+
+def test_trace_two_slot_schedule_image():
+    wl = synth.workload("image")
+    shapes = list(wl.blocks[:8])
+    W = _weights(wl, range(8))
+    ctx = _ctx(shapes, 4, wl.tokens, flags=dlo.FLAG_TRACE)
+    for b in range(8):
+        ctx.load_shards(b, W[b])
+    x = synth.activations(wl.tokens, 2048)
+    _run(ctx, x, synth.conditioning(256))
+    tr = ctx.trace()
+    st = ctx.stats()
+    numels = [OL.block_numel(s) for s in shapes]
+    errs = OT.check_trace(tr, 8, slot_capacity=st["slot_bytes"] // 2, numels=numels, dp=4)
+    assert errs == [], errs[:5]
+    assert OT.residency_high_water(tr, 8) <= 2
+    assert st["residency_high_water"] <= 2
+    assert st["slot_bytes"] == 2 * OT.slot_capacity_elems(numels, 4)
+    print("stats", st)
+
+
+# ------------------------------------------------------------------ errors
+
+def test_errors_fail_closed():
+    t = torch()
+    wl = synth.workload("tiny")
+    ctx = _ctx(list(wl.blocks), 4, wl.tokens)
+    xbuf = t.zeros(wl.tokens * 256, dtype=t.float32, device="cuda")
+    cond = dev(synth.conditioning(256))
+    assert ctx.forward_status(xbuf, cond, wl.tokens) == dlo.E_STATE  # nothing loaded
+    W = _weights(wl)
+    with pytest.raises(dlo.DloError) as e:
+        ctx.load_shards(0, W[0][:-1])
+    assert e.value.code == dlo.E_SHAPE
+    for b, flat in W.items():
+        ctx.load_shards(b, flat)
+    assert ctx.forward_status(xbuf, cond, 0) == dlo.E_INVAL
+    assert ctx.forward_status(xbuf, cond, wl.tokens + 1) == dlo.E_INVAL
+    assert ctx.forward_status(None, cond, wl.tokens) == dlo.E_INVAL
+    assert ctx.forward_status(xbuf, cond, wl.tokens) == dlo.OK
+    t.cuda.synchronize()

@@ -1,0 +1,159 @@
+"""Each kernel against the oracle's definition of its step, on seeded inputs
+that span several tiles and a ragged tail.  Calls go through the C ABI."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import dit as D
+from gpu_util import dev, host, bf16_to_f64, within, torch
+
+pytestmark = pytest.mark.gpu
+
+import layerwise_weight_streaming_dit_amd as dlo
+
+
+def _bf16(a):
+    return synth.bf16_bits_from_f32(np.asarray(a, np.float32))
+
+
+# ------------------------------------------------------------- reconstruction
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 4095, 65536 + 13, (1 << 21) + 5])
+@pytest.mark.parametrize("dst_off,src_off", [(0, 0), (3, 3), (5, 5), (1, 6), (7, 0)])
+def test_assemble_bit_exact(n, dst_off, src_off):
+    rng = np.random.default_rng(n + 31 * dst_off + src_off)
+    src = rng.integers(0, 1 << 16, size=n + 16, dtype=np.uint16)
+    t = torch()
+    s = dev(src)
+    d = t.full((n + 16,), -1, dtype=t.int16, device="cuda")
+    dlo.op_assemble(d[dst_off:], s[src_off:], n)
+    t.cuda.synchronize()
+    out = host(d, np.uint16)
+    assert np.array_equal(out[dst_off:dst_off + n], src[src_off:src_off + n])
+    assert np.all(out[:dst_off] == 0xFFFF) and np.all(out[dst_off + n:] == 0xFFFF)
+
+
+# ------------------------------------------------------------------- adaLN
+
+@pytest.mark.parametrize("d,c", [(256, 256), (2048, 256), (3072, 64)])
+def test_adaln(d, c):
+    rng = np.random.default_rng(d + c)
+    w = _bf16(rng.standard_normal((6 * d, c)) * 0.02)
+    b = _bf16(rng.standard_normal(6 * d) * 0.02)
+    cond = rng.standard_normal(c).astype(np.float32)
+    t = torch()
+    mod = t.empty(6 * d, dtype=t.float32, device="cuda")
+    dlo.op_adaln(dev(w), dev(b), dev(cond), mod, 6 * d, c)
+    want = bf16_to_f64(w).reshape(6 * d, c) @ D.silu(cond.astype(np.float64)) + bf16_to_f64(b)
+    ok, ma, mr = within(host(mod), want, rtol=1e-4, atol=1e-5)
+    assert ok, (ma, mr)
+
+
+# ------------------------------------------------------- LayerNorm + modulate
+
+@pytest.mark.parametrize("tokens,d_in,d", [(1, 256, 256), (37, 2048, 2048), (300, 3072, 4096),
+                                           (65, 4096, 3072), (8, 8192, 8192)])
+def test_ln_modulate(tokens, d_in, d):
+    rng = np.random.default_rng(tokens * d)
+    x = (rng.standard_normal((tokens, d_in)) * 2 + 0.5).astype(np.float32)
+    shift = rng.standard_normal(d).astype(np.float32) * 0.3
+    scale = rng.standard_normal(d).astype(np.float32) * 0.3
+    t = torch()
+    h = t.empty((tokens, d), dtype=t.int16, device="cuda")
+    xo = t.full((tokens, d), float("nan"), dtype=t.float32, device="cuda") if d_in != d else None
+    dlo.op_ln_modulate(dev(x), d_in, xo, dev(shift), dev(scale), h, tokens, d)
+    y = D.width_adapter(x.astype(np.float64), d)
+    want = D.modulate(D.layer_norm(y), shift.astype(np.float64), scale.astype(np.float64))
+    ok, ma, mr = within(bf16_to_f64(host(h, np.uint16)), want, rtol=8e-3, atol=1e-3)
+    assert ok, (ma, mr)
+    if xo is not None:
+        assert np.array_equal(host(xo), y.astype(np.float32))
+
+
+# --------------------------------------------------------------------- GEMM
+
+def _gemm_case(epi, M, N, K, w_rows=None, seed=0):
+    rng = np.random.default_rng(seed)
+    w_rows = N if w_rows is None else w_rows
+    a = _bf16(rng.standard_normal((M, K)))
+    w = _bf16(rng.standard_normal((w_rows, K)) * 0.02)
+    nb = M if epi == dlo.EPI_ROWBIAS_BF16 else N
+    bias = _bf16(rng.standard_normal(nb) * 0.1)
+    gate = rng.standard_normal(N).astype(np.float32)
+    x0 = rng.standard_normal((M, N)).astype(np.float32)
+    t = torch()
+    if epi == dlo.EPI_GATED_F32:
+        out = dev(x0.copy())
+    else:
+        out = t.empty((M, N), dtype=t.int16, device="cuda")
+    dlo.op_gemm(epi, dev(a), K, dev(w), K, w_rows, dev(bias), dev(gate), out, N, M, N, K)
+    wf = bf16_to_f64(w)
+    wfull = wf[np.minimum(np.arange(N), w_rows - 1)]
+    acc = bf16_to_f64(a) @ wfull.T
+    bf = bf16_to_f64(bias)
+    if epi == dlo.EPI_BIAS_BF16:
+        return bf16_to_f64(host(out, np.uint16)), acc + bf
+    if epi == dlo.EPI_BIAS_GELU_BF16:
+        return bf16_to_f64(host(out, np.uint16)), D.gelu_tanh(acc + bf)
+    if epi == dlo.EPI_GATED_F32:
+        return host(out).astype(np.float64), x0 + gate.astype(np.float64) * (acc + bf)
+    return bf16_to_f64(host(out, np.uint16)), acc + bf[:, None]
+
+
+@pytest.mark.parametrize("epi", [dlo.EPI_BIAS_BF16, dlo.EPI_BIAS_GELU_BF16, dlo.EPI_GATED_F32, dlo.EPI_ROWBIAS_BF16])
+@pytest.mark.parametrize("M,N,K", [(256, 768, 256), (300, 256, 1024), (1000, 512, 512), (4096 + 17, 2048, 256),
+                                   (33, 128, 64)])
+def test_gemm(epi, M, N, K):
+    got, want = _gemm_case(epi, M, N, K, seed=M + N + K + epi)
+    ok, ma, mr = within(got, want, rtol=1e-2, atol=1e-2)
+    assert ok, (ma, mr)
+
+
+def test_gemm_clamped_w_rows():
+    # the transposed v projection: output columns past w_rows repeat the last row
+    got, want = _gemm_case(dlo.EPI_ROWBIAS_BF16, 512, 1088, 256, w_rows=1000, seed=5)
+    ok, ma, mr = within(got, want, rtol=1e-2, atol=1e-2)
+    assert ok, (ma, mr)
+
+
+def test_gemm_large_tile_shapes():
+    # shapes that select the 256x256 and 256x128 tiles
+    for (M, N, K) in [(4096, 4096, 512), (4096, 2048, 512)]:
+        got, want = _gemm_case(dlo.EPI_BIAS_BF16, M, N, K, seed=M + N)
+        ok, ma, mr = within(got, want, rtol=1e-2, atol=1e-2)
+        assert ok, (M, N, K, ma, mr)
+
+
+# ---------------------------------------------------------------- attention
+
+def _attention_case(T, H, hd, qscale=1.0, seed=0):
+    rng = np.random.default_rng(seed)
+    d = H * hd
+    q = _bf16(rng.standard_normal((T, d)) * qscale)
+    k = _bf16(rng.standard_normal((T, d)))
+    v = _bf16(rng.standard_normal((T, d)))
+    tp = (T + 63) // 64 * 64
+    vt = np.zeros((d, tp), np.uint16)
+    vt[:, :T] = v.T
+    qk = np.concatenate([q, k], axis=1)
+    t = torch()
+    o = t.empty((T, d), dtype=t.int16, device="cuda")
+    dlo.op_attention(dev(qk), 2 * d, dev(vt), tp, o, d, T, H, hd)
+    want = D.attention(bf16_to_f64(q), bf16_to_f64(k), bf16_to_f64(v), H)
+    return bf16_to_f64(host(o, np.uint16)), want
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 129, 200, 1000])
+@pytest.mark.parametrize("H,hd", [(2, 64), (2, 128)])
+def test_attention(T, H, hd):
+    got, want = _attention_case(T, H, hd, seed=T * hd)
+    ok, ma, mr = within(got, want, rtol=2e-2, atol=2e-2)
+    assert ok, (ma, mr)
+    assert ma < 2e-2
+
+
+@pytest.mark.parametrize("qscale", [4.0, 30.0])
+def test_attention_peaked_softmax(qscale):
+    got, want = _attention_case(300, 2, 128, qscale=qscale, seed=7)
+    ok, ma, mr = within(got, want)
+    assert ok, (ma, mr)
