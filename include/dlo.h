@@ -86,6 +86,9 @@ typedef int32_t dlo_status;
 #define DLO_FLAG_POISON_SLOTS 0x4u /* test hook: fill a slot with bf16 NaN
                                       before reconstructing into it, so a read
                                       ahead of the reconstruction shows up */
+#define DLO_FLAG_TRACE_KERNELS 0x8u /* record only the compute-stream intervals
+                                       (block compute and each kernel): keeps
+                                       events off the copy and gather streams */
 
 typedef struct dlo_ctx dlo_ctx;
 
@@ -132,16 +135,27 @@ typedef struct dlo_param_desc {
   int64_t shape[2];
 } dlo_param_desc;
 
-/* One timed interval of the streaming schedule (DLO_FLAG_TRACE). */
+/* One timed interval of the streaming schedule (DLO_FLAG_TRACE): per H2D
+ * chunk, per reconstruction chunk, per block compute and per kernel. */
 #define DLO_IV_H2D 0
 #define DLO_IV_ASM 1
 #define DLO_IV_COMPUTE 2
+/* kernels inside a block's compute interval (compute stream) */
+#define DLO_IV_K_ADALN 3   /* adaLN modulation vector */
+#define DLO_IV_K_LN1 4     /* LayerNorm + modulate before attention */
+#define DLO_IV_K_QK 5      /* q, k projection GEMM */
+#define DLO_IV_K_V 6       /* v projection GEMM (transposed output) */
+#define DLO_IV_K_ATTN 7    /* attention */
+#define DLO_IV_K_OUT 8     /* output projection GEMM + gated residual */
+#define DLO_IV_K_LN2 9     /* LayerNorm + modulate before the MLP */
+#define DLO_IV_K_FC1 10    /* MLP up GEMM + GELU */
+#define DLO_IV_K_FC2 11    /* MLP down GEMM + gated residual */
 typedef struct dlo_interval {
   int32_t kind;      /* DLO_IV_* */
   int32_t block;     /* block index */
-  int32_t chunk;     /* chunk index within the block, -1 for compute */
+  int32_t chunk;     /* chunk index within the block, -1 otherwise */
   int32_t slot;      /* slot written (ASM) or read (COMPUTE), -1 for H2D */
-  int32_t landing;   /* landing buffer written (H2D) or read (ASM), -1 for compute */
+  int32_t landing;   /* landing buffer written (H2D) or read (ASM), -1 otherwise */
   int32_t reserved;
   int64_t bytes;     /* bytes moved (H2D, ASM reads) or 0 */
   double start_ms;   /* relative to the start of the forward */

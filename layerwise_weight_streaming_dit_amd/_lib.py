@@ -21,9 +21,10 @@ ABI_VERSION = 1
 OK, E_INVAL, E_SHAPE, E_STATE, E_HOST_OOM, E_DEV_OOM, E_HIP, E_POISONED = 0, -1, -2, -3, -4, -5, -6, -7
 STATUS_NAMES = {0: "DLO_OK", -1: "DLO_E_INVAL", -2: "DLO_E_SHAPE", -3: "DLO_E_STATE", -4: "DLO_E_HOST_OOM",
                 -5: "DLO_E_DEV_OOM", -6: "DLO_E_HIP", -7: "DLO_E_POISONED"}
-FLAG_TRACE, FLAG_SERIALIZE, FLAG_POISON_SLOTS = 0x1, 0x2, 0x4
+FLAG_TRACE, FLAG_SERIALIZE, FLAG_POISON_SLOTS, FLAG_TRACE_KERNELS = 0x1, 0x2, 0x4, 0x8
 IV_H2D, IV_ASM, IV_COMPUTE = 0, 1, 2
-IV_NAMES = {0: "h2d", 1: "asm", 2: "compute"}
+IV_NAMES = {0: "h2d", 1: "asm", 2: "compute", 3: "k_adaln", 4: "k_ln1", 5: "k_qk", 6: "k_v", 7: "k_attn",
+            8: "k_out", 9: "k_ln2", 10: "k_fc1", 11: "k_fc2"}
 EPI_BIAS_BF16, EPI_BIAS_GELU_BF16, EPI_GATED_F32, EPI_ROWBIAS_BF16 = 0, 1, 2, 3
 
 

@@ -226,8 +226,9 @@ hipEvent_t next_ev(dlo_ctx* ctx) {
 }
 
 // Enqueue the H2D + reconstruction of block b into slot b % 2 on the copy and
-// gather streams.  `trace` adds timed intervals.
-dlo_status enqueue_staging(dlo_ctx* ctx, int b, bool trace, hipStream_t compute_s) {
+// gather streams.  `trace` adds timed intervals; `in_forward` is false for
+// the stand-alone debug path (no compute of block b-1 to wait for).
+dlo_status enqueue_staging(dlo_ctx* ctx, int b, bool trace, bool in_forward) {
   Block& blk = ctx->blocks[b];
   const int k = b & 1;
   for (size_t ci = 0; ci < blk.chunks.size(); ++ci) {
@@ -238,7 +239,7 @@ dlo_status enqueue_staging(dlo_ctx* ctx, int b, bool trace, hipStream_t compute_
     uint16_t* land = ctx->landing[lb] + co;
     // copy stream
     DLO_HIP(ctx, hipStreamWaitEvent(ctx->copy_s, ctx->land_free[lb], 0));
-    if ((ctx->flags & DLO_FLAG_SERIALIZE) && ci == 0 && compute_s != nullptr) {
+    if ((ctx->flags & DLO_FLAG_SERIALIZE) && ci == 0 && in_forward) {
       // synchronous schedule: nothing of block b moves before block b-1 computed
       DLO_HIP(ctx, hipStreamWaitEvent(ctx->copy_s, ctx->comp_done[k ^ 1], 0));
     }
@@ -279,7 +280,7 @@ dlo_status enqueue_staging(dlo_ctx* ctx, int b, bool trace, hipStream_t compute_
 
 // The DiT block of `b` from slot b % 2 on the compute stream.
 dlo_status enqueue_block_compute(dlo_ctx* ctx, int b, float*& x_cur, int& d_cur, float* x_user,
-                                 const float* cond, int T, hipStream_t s) {
+                                 const float* cond, int T, hipStream_t s, bool trace) {
   const Block& blk = ctx->blocks[b];
   const BlockLayout& L = blk.layout;
   const uint16_t* base = ctx->slot[b & 1];
@@ -299,34 +300,53 @@ dlo_status enqueue_block_compute(dlo_ctx* ctx, int b, float*& x_cur, int& d_cur,
   const int Tp = static_cast<int>(align_up(size_t(T), 64));
   const Workspace& w = ctx->ws;
   float* mod = w.mod;
+  const int k = b & 1;
+  // Record a timed interval around one kernel when tracing.
+  auto timed = [&](int kind, auto&& launch) -> dlo_status {
+    TraceEv tv{};
+    if (trace) {
+      tv = TraceEv{kind, b, -1, k, -1, 0, next_ev(ctx), next_ev(ctx)};
+      if (tv.start) DLO_HIP(ctx, hipEventRecord(tv.start, s));
+    }
+    DLO_HIP(ctx, launch());
+    if (trace && tv.end) {
+      DLO_HIP(ctx, hipEventRecord(tv.end, s));
+      ctx->trace.push_back(tv);
+    }
+    return DLO_OK;
+  };
+  dlo_status st;
+#define DLO_STEP(kind, expr)                       \
+  st = timed(kind, [&]() -> hipError_t { return (expr); }); \
+  if (st != DLO_OK) return st
 
-  DLO_HIP(ctx, launch_adaln(Wada, bada, cond, mod, 6 * d, c, s));
+  DLO_STEP(DLO_IV_K_ADALN, launch_adaln(Wada, bada, cond, mod, 6 * d, c, s));
   if (d != d_cur) {
     float* x_new = (x_cur == x_user) ? w.xalt : x_user;
-    DLO_HIP(ctx, launch_ln_modulate(x_cur, d_cur, x_new, mod, mod + d, w.h, T, d, s));
+    DLO_STEP(DLO_IV_K_LN1, launch_ln_modulate(x_cur, d_cur, x_new, mod, mod + d, w.h, T, d, s));
     x_cur = x_new;
     d_cur = d;
   } else {
-    DLO_HIP(ctx, launch_ln_modulate(x_cur, d, nullptr, mod, mod + d, w.h, T, d, s));
+    DLO_STEP(DLO_IV_K_LN1, launch_ln_modulate(x_cur, d, nullptr, mod, mod + d, w.h, T, d, s));
   }
-  GemmArgs g{};
   // q, k projection: qk[T][2d] = h Wqk^T + bqk
-  g = GemmArgs{w.h, Wqkv, bqkv, nullptr, w.qk, d, d, 2 * d, T, 2 * d, d, 2 * d};
-  DLO_HIP(ctx, launch_gemm(EPI_BIAS_BF16, g, s));
+  const GemmArgs gqk{w.h, Wqkv, bqkv, nullptr, w.qk, d, d, 2 * d, T, 2 * d, d, 2 * d};
+  DLO_STEP(DLO_IV_K_QK, launch_gemm(EPI_BIAS_BF16, gqk, s));
   // v projection, transposed: vt[d][Tp] = Wv h^T + bv (columns >= T finite)
-  g = GemmArgs{Wqkv + int64_t(2) * d * d, w.h, bqkv + 2 * d, nullptr, w.vt, d, d, Tp, d, Tp, d, T};
-  DLO_HIP(ctx, launch_gemm(EPI_ROWBIAS_BF16, g, s));
-  DLO_HIP(ctx, launch_attention(w.qk, 2 * d, w.vt, Tp, w.o, d, T, H, hd, s));
+  const GemmArgs gv{Wqkv + int64_t(2) * d * d, w.h, bqkv + 2 * d, nullptr, w.vt, d, d, Tp, d, Tp, d, T};
+  DLO_STEP(DLO_IV_K_V, launch_gemm(EPI_ROWBIAS_BF16, gv, s));
+  DLO_STEP(DLO_IV_K_ATTN, launch_attention(w.qk, 2 * d, w.vt, Tp, w.o, d, T, H, hd, s));
   // x += gate1 * (o Wo^T + bo)
-  g = GemmArgs{w.o, Wo, bo, mod + 2 * d, x_cur, d, d, d, T, d, d, d};
-  DLO_HIP(ctx, launch_gemm(EPI_GATED_F32, g, s));
-  DLO_HIP(ctx, launch_ln_modulate(x_cur, d, nullptr, mod + 3 * d, mod + 4 * d, w.h, T, d, s));
+  const GemmArgs go{w.o, Wo, bo, mod + 2 * d, x_cur, d, d, d, T, d, d, d};
+  DLO_STEP(DLO_IV_K_OUT, launch_gemm(EPI_GATED_F32, go, s));
+  DLO_STEP(DLO_IV_K_LN2, launch_ln_modulate(x_cur, d, nullptr, mod + 3 * d, mod + 4 * d, w.h, T, d, s));
   // u = gelu(h2 W1^T + b1)
-  g = GemmArgs{w.h, W1, b1, nullptr, w.u, d, d, m, T, m, d, m};
-  DLO_HIP(ctx, launch_gemm(EPI_BIAS_GELU_BF16, g, s));
+  const GemmArgs g1{w.h, W1, b1, nullptr, w.u, d, d, m, T, m, d, m};
+  DLO_STEP(DLO_IV_K_FC1, launch_gemm(EPI_BIAS_GELU_BF16, g1, s));
   // x += gate2 * (u W2^T + b2)
-  g = GemmArgs{w.u, W2, b2, mod + 5 * d, x_cur, m, m, d, T, d, m, d};
-  DLO_HIP(ctx, launch_gemm(EPI_GATED_F32, g, s));
+  const GemmArgs g2{w.u, W2, b2, mod + 5 * d, x_cur, m, m, d, T, d, m, d};
+  DLO_STEP(DLO_IV_K_FC2, launch_gemm(EPI_GATED_F32, g2, s));
+#undef DLO_STEP
   return DLO_OK;
 }
 
@@ -469,9 +489,9 @@ extern "C" DLO_API dlo_status dlo_create(const dlo_config* cfg, dlo_ctx** out) {
     DLO_HIP(nullptr, hipEventRecord(c->land_free[i], c->gather_s));
     DLO_HIP(nullptr, hipEventRecord(c->comp_done[i], c->gather_s));
   }
-  if (c->flags & DLO_FLAG_TRACE) {
+  if (c->flags & (DLO_FLAG_TRACE | DLO_FLAG_TRACE_KERNELS)) {
     size_t n = 0;
-    for (auto& b : c->blocks) n += 4 * b.chunks.size() + 2;
+    for (auto& b : c->blocks) n += 4 * b.chunks.size() + 2 + 2 * 9;
     c->ev_pool.resize(n, nullptr);
     for (size_t i = 0; i < n; ++i) DLO_HIP(nullptr, hipEventCreate(&c->ev_pool[i]));
   }
@@ -539,7 +559,8 @@ extern "C" DLO_API dlo_status dlo_forward(dlo_ctx* ctx, float* x, const float* c
   DeviceGuard dg(ctx->device);
   if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
 
-  const bool trace = (ctx->flags & DLO_FLAG_TRACE) != 0;
+  const bool trace_all = (ctx->flags & DLO_FLAG_TRACE) != 0;
+  const bool trace = trace_all || (ctx->flags & DLO_FLAG_TRACE_KERNELS) != 0;
   if (trace) {
     ctx->trace.clear();
     ctx->ev_next = 0;
@@ -549,7 +570,7 @@ extern "C" DLO_API dlo_status dlo_forward(dlo_ctx* ctx, float* x, const float* c
   int d_cur = ctx->blocks[0].desc.d_model;
   const int L = static_cast<int>(ctx->blocks.size());
   for (int b = 0; b < L; ++b) {
-    st = enqueue_staging(ctx, b, trace, stream);
+    st = enqueue_staging(ctx, b, trace_all, true);
     if (st != DLO_OK) return st;
     const int k = b & 1;
     DLO_HIP(ctx, hipStreamWaitEvent(stream, ctx->asm_done[k], 0));
@@ -558,7 +579,7 @@ extern "C" DLO_API dlo_status dlo_forward(dlo_ctx* ctx, float* x, const float* c
       tc = TraceEv{DLO_IV_COMPUTE, b, -1, k, -1, 0, next_ev(ctx), next_ev(ctx)};
       if (tc.start) DLO_HIP(ctx, hipEventRecord(tc.start, stream));
     }
-    st = enqueue_block_compute(ctx, b, x_cur, d_cur, x, cond, tokens, stream);
+    st = enqueue_block_compute(ctx, b, x_cur, d_cur, x, cond, tokens, stream, trace);
     if (st != DLO_OK) return st;
     if (trace && tc.end) {
       DLO_HIP(ctx, hipEventRecord(tc.end, stream));
@@ -632,7 +653,7 @@ extern "C" DLO_API dlo_status dlo_debug_assemble(dlo_ctx* ctx, int32_t block, ui
     return fail(DLO_E_INVAL, "host_out must hold %lld elements", (long long)b.layout.numel);
   DeviceGuard dg(ctx->device);
   if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
-  st = enqueue_staging(ctx, block, false, nullptr);
+  st = enqueue_staging(ctx, block, false, false);
   if (st != DLO_OK) return st;
   DLO_HIP(ctx, hipStreamSynchronize(ctx->gather_s));
   DLO_HIP(ctx, hipMemcpy(host_out, ctx->slot[block & 1], size_t(b.layout.numel) * 2, hipMemcpyDeviceToHost));
@@ -701,6 +722,7 @@ dlo_status collect_trace(dlo_ctx* ctx, std::vector<dlo_interval>& out, dlo_stats
     }
     std::vector<std::pair<double, int>> evs;
     for (int b2 = 0; b2 < L; ++b2) {
+      if (first[b2] > 1e299 || last[b2] < -1e299) continue;  // schedule not traced
       evs.push_back({first[b2], 1});
       evs.push_back({last[b2], -1});
     }

@@ -259,3 +259,40 @@ def test_errors_fail_closed():
     assert ctx.forward_status(None, cond, wl.tokens) == dlo.E_INVAL
     assert ctx.forward_status(xbuf, cond, wl.tokens) == dlo.OK
     t.cuda.synchronize()
+
+
+def test_serialized_schedule_really_serializes():
+    wl = synth.workload("tiny")
+    W = _weights(wl)
+    ctx = _ctx(list(wl.blocks), 4, wl.tokens, flags=dlo.FLAG_TRACE | dlo.FLAG_SERIALIZE)
+    for b, flat in W.items():
+        ctx.load_shards(b, flat)
+    _run(ctx, synth.activations(wl.tokens, 256), synth.conditioning(256))
+    tr = ctx.trace()
+    assert OT.check_trace(tr, wl.num_blocks) == []
+    comp_end = {r["block"]: r["end"] for r in tr if r["kind"] == "compute"}
+    for r in tr:
+        if r["kind"] == "h2d" and r["block"] >= 1:
+            assert r["start"] >= comp_end[r["block"] - 1]
+
+
+def test_kernel_trace_covers_every_step():
+    wl = synth.workload("tiny")
+    W = _weights(wl)
+    ctx = _ctx(list(wl.blocks), 4, wl.tokens, flags=dlo.FLAG_TRACE_KERNELS)
+    for b, flat in W.items():
+        ctx.load_shards(b, flat)
+    _run(ctx, synth.activations(wl.tokens, 256), synth.conditioning(256))
+    tr = ctx.trace()
+    kinds = {}
+    for r in tr:
+        kinds.setdefault(r["kind"], []).append(r)
+    assert "h2d" not in kinds and "asm" not in kinds
+    for k in ("compute", "k_adaln", "k_ln1", "k_qk", "k_v", "k_attn", "k_out", "k_ln2", "k_fc1", "k_fc2"):
+        assert len(kinds[k]) == wl.num_blocks, k
+    comp = {r["block"]: r for r in kinds["compute"]}
+    for k, rs in kinds.items():
+        if k.startswith("k_"):
+            for r in rs:
+                c = comp[r["block"]]
+                assert c["start"] <= r["start"] <= r["end"] <= c["end"]
