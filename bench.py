@@ -225,7 +225,20 @@ def main():
         if r["kind"].startswith("k_"):
             by.setdefault(r["kind"], []).append(r)
     dur = lambda rs: sum(r["end"] - r["start"] for r in rs)
-    h2d_ms, asm_ms, comp_ms = dur(by.get("h2d", [])), dur(by.get("asm", [])), dur(by.get("compute", []))
+
+    def busy(rs):
+        # length of the union of intervals (the two copy engines overlap)
+        tot, cs, ce = 0.0, None, None
+        for r in sorted(rs, key=lambda r: r["start"]):
+            if ce is None or r["start"] > ce:
+                if ce is not None:
+                    tot += ce - cs
+                cs, ce = r["start"], r["end"]
+            else:
+                ce = max(ce, r["end"])
+        return tot + (ce - cs if ce is not None else 0.0)
+
+    h2d_ms, asm_ms, comp_ms = busy(by.get("h2d", [])), busy(by.get("asm", [])), busy(by.get("compute", []))
     t_fwd = max(r["end"] for r in tr) - min(r["start"] for r in tr)
     h2d_bytes = sum(r["bytes"] for r in by.get("h2d", []))
     asm_read = sum(r["bytes"] for r in by.get("asm", []))

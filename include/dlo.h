@@ -120,8 +120,10 @@ typedef struct dlo_config {
                                   aligned, at least dlo_required_bytes' total;
                                   must stay alive until dlo_destroy */
   size_t arena_bytes;
-  hipStream_t copy_stream;     /* side stream for H2D copies; NULL = the
-                                  library creates its own */
+  hipStream_t copy_stream;     /* side stream for the H2D copies of even
+                                  chunks; NULL = the library creates its own.
+                                  Odd chunks go on a second copy stream the
+                                  library always owns (a second DMA engine) */
   hipStream_t gather_stream;   /* side stream for reconstruction; NULL = the
                                   library creates its own */
 } dlo_config;
@@ -174,7 +176,7 @@ typedef struct dlo_stats {
                                   the last traced forward (0 if untraced) */
   int32_t n_intervals;         /* intervals recorded by the last traced forward */
   double last_forward_ms;      /* first H2D start to last compute end (traced) */
-  double sum_h2d_ms;           /* summed busy time per stream (traced) */
+  double sum_h2d_ms;           /* busy time (union of intervals) per kind (traced) */
   double sum_asm_ms;
   double sum_compute_ms;
   int64_t h2d_bytes_per_forward;

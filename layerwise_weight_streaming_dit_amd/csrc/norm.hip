@@ -9,7 +9,6 @@ namespace dlo {
 namespace {
 
 constexpr int kNormThreads = 256;
-constexpr int kMaxVec = 8;  // float4 per thread: d <= 8 * 4 * 256 = 8192
 constexpr int kAdaRowsPerWave = 4;
 
 // mod[r] = W[r] . silu(cond) + b[r].  silu(cond) is staged once per workgroup
@@ -40,6 +39,7 @@ __global__ __launch_bounds__(kNormThreads) void adaln_kernel(const uint16_t* __r
   }
 }
 
+template <int THREADS>
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -48,43 +48,46 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   __syncthreads();
   float t = 0.f;
 #pragma unroll
-  for (int i = 0; i < kNormThreads / 64; ++i) t += red[i];
+  for (int i = 0; i < THREADS / 64; ++i) t += red[i];
   return t;
 }
 
 // One workgroup per token row.  The row (adapted to width d) is held in
-// registers; mean and variance are two passes over the registers.
-__global__ __launch_bounds__(kNormThreads) void ln_modulate_kernel(
+// registers, at most two float4 per thread (the workgroup grows with d, up to
+// 1024 threads for d = 8192, so registers stay few and occupancy high); mean
+// and variance are two passes over the registers.
+template <int THREADS, int NV>
+__global__ __launch_bounds__(THREADS) void ln_modulate_kernel(
     const float* __restrict__ xin, int d_in, float* __restrict__ xout, const float* __restrict__ shift,
     const float* __restrict__ scale, uint16_t* __restrict__ h, int d) {
-  __shared__ float red[kNormThreads / 64];
+  __shared__ float red[THREADS / 64];
   const int64_t t = blockIdx.x;
   const float* xr = xin + t * d_in;
   const int nv = d / 4;
-  f32x4_t v[kMaxVec];
+  f32x4_t v[NV];
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxVec; ++i) {
-    const int q = threadIdx.x + i * kNormThreads;
+  for (int i = 0; i < NV; ++i) {
+    const int q = threadIdx.x + i * THREADS;
     v[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (q < nv && q * 4 < d_in) v[i] = *reinterpret_cast<const f32x4_t*>(xr + q * 4);
     s += v[i].x + v[i].y + v[i].z + v[i].w;
   }
-  const float mean = block_sum(s, red) / static_cast<float>(d);
+  const float mean = block_sum<THREADS>(s, red) / static_cast<float>(d);
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxVec; ++i) {
-    const int q = threadIdx.x + i * kNormThreads;
+  for (int i = 0; i < NV; ++i) {
+    const int q = threadIdx.x + i * THREADS;
     if (q < nv) {
       const f32x4_t e = v[i] - mean;
       ss += e.x * e.x + e.y * e.y + e.z * e.z + e.w * e.w;
     }
   }
-  const float var = block_sum(ss, red) / static_cast<float>(d);
+  const float var = block_sum<THREADS>(ss, red) / static_cast<float>(d);
   const float rstd = rsqrtf(var + 1e-6f);
 #pragma unroll
-  for (int i = 0; i < kMaxVec; ++i) {
-    const int q = threadIdx.x + i * kNormThreads;
+  for (int i = 0; i < NV; ++i) {
+    const int q = threadIdx.x + i * THREADS;
     if (q < nv) {
       const f32x4_t sh = *reinterpret_cast<const f32x4_t*>(shift + q * 4);
       const f32x4_t sc = *reinterpret_cast<const f32x4_t*>(scale + q * 4);
@@ -111,8 +114,15 @@ hipError_t launch_adaln(const uint16_t* w, const uint16_t* b, const float* cond,
 hipError_t launch_ln_modulate(const float* xin, int d_in, float* xout, const float* shift,
                               const float* scale, uint16_t* h, int tokens, int d, hipStream_t s) {
   if (tokens <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ln_modulate_kernel, dim3(tokens), dim3(kNormThreads), 0, s, xin, d_in, xout,
-                     shift, scale, h, d);
+  const dim3 grid(tokens);
+  if (d <= 1024)
+    hipLaunchKernelGGL((ln_modulate_kernel<256, 1>), grid, dim3(256), 0, s, xin, d_in, xout, shift, scale, h, d);
+  else if (d <= 2048)
+    hipLaunchKernelGGL((ln_modulate_kernel<256, 2>), grid, dim3(256), 0, s, xin, d_in, xout, shift, scale, h, d);
+  else if (d <= 4096)
+    hipLaunchKernelGGL((ln_modulate_kernel<512, 2>), grid, dim3(512), 0, s, xin, d_in, xout, shift, scale, h, d);
+  else
+    hipLaunchKernelGGL((ln_modulate_kernel<1024, 2>), grid, dim3(1024), 0, s, xin, d_in, xout, shift, scale, h, d);
   return hipGetLastError();
 }
 

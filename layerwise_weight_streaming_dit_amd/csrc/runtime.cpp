@@ -16,10 +16,12 @@
 // One GPU plays every rank here: all dp shards of a block are copied, in
 // chunks, through two landing buffers (the per-rank receive buffers), and the
 // reconstruction kernel copies each landed chunk to its place in the slot,
-// dropping the zero padding.
+// dropping the zero padding.  Chunks alternate between two copy streams (two
+// DMA engines), one per landing buffer: while one engine sets up its next
+// transfer the other keeps the host link busy.
 //
 // Per block b (slot k = b % 2) the host enqueues, without ever blocking:
-//   copy stream   : per chunk j: wait land_free[j%2]; H2D -> landing[j%2];
+//   copy stream j%2: per chunk j: wait land_free[j%2]; H2D -> landing[j%2];
 //                   record h2d_done[j%2]
 //   gather stream : wait comp_done[k] (compute of block b-2 released slot k);
 //                   per chunk j: wait h2d_done[j%2]; reconstruct into slot k;
@@ -99,7 +101,7 @@ struct dlo_ctx {
   uint16_t* slot[2] = {nullptr, nullptr};
   uint16_t* landing[2] = {nullptr, nullptr};
   dlo::Workspace ws;
-  hipStream_t copy_s = nullptr, gather_s = nullptr;
+  hipStream_t copy_s = nullptr, copy_s2 = nullptr, gather_s = nullptr;
   bool own_copy = false, own_gather = false;
   hipEvent_t h2d_done[2] = {}, land_free[2] = {}, asm_done[2] = {}, comp_done[2] = {};
   int64_t land_counter = 0;  // global chunk counter (landing buffer parity)
@@ -237,24 +239,25 @@ dlo_status enqueue_staging(dlo_ctx* ctx, int b, bool trace, bool in_forward) {
     ++ctx->land_counter;
     const int64_t co = c.dst % kLandSlack;  // co-align landing with slot (mod 16 bytes)
     uint16_t* land = ctx->landing[lb] + co;
-    // copy stream
-    DLO_HIP(ctx, hipStreamWaitEvent(ctx->copy_s, ctx->land_free[lb], 0));
-    if ((ctx->flags & DLO_FLAG_SERIALIZE) && ci == 0 && in_forward) {
+    hipStream_t cs = lb ? ctx->copy_s2 : ctx->copy_s;
+    // copy stream of this landing buffer
+    DLO_HIP(ctx, hipStreamWaitEvent(cs, ctx->land_free[lb], 0));
+    if ((ctx->flags & DLO_FLAG_SERIALIZE) && in_forward) {
       // synchronous schedule: nothing of block b moves before block b-1 computed
-      DLO_HIP(ctx, hipStreamWaitEvent(ctx->copy_s, ctx->comp_done[k ^ 1], 0));
+      DLO_HIP(ctx, hipStreamWaitEvent(cs, ctx->comp_done[k ^ 1], 0));
     }
     TraceEv tv{};
     if (trace) {
       tv = TraceEv{DLO_IV_H2D, b, static_cast<int>(ci), -1, lb, c.len * 2, next_ev(ctx), next_ev(ctx)};
-      if (tv.start) DLO_HIP(ctx, hipEventRecord(tv.start, ctx->copy_s));
+      if (tv.start) DLO_HIP(ctx, hipEventRecord(tv.start, cs));
     }
     DLO_HIP(ctx, hipMemcpyAsync(land, blk.shards[c.rank] + c.src_off, size_t(c.len) * 2,
-                                hipMemcpyHostToDevice, ctx->copy_s));
+                                hipMemcpyHostToDevice, cs));
     if (trace && tv.end) {
-      DLO_HIP(ctx, hipEventRecord(tv.end, ctx->copy_s));
+      DLO_HIP(ctx, hipEventRecord(tv.end, cs));
       ctx->trace.push_back(tv);
     }
-    DLO_HIP(ctx, hipEventRecord(ctx->h2d_done[lb], ctx->copy_s));
+    DLO_HIP(ctx, hipEventRecord(ctx->h2d_done[lb], cs));
     // gather stream
     if (ci == 0) {
       DLO_HIP(ctx, hipStreamWaitEvent(ctx->gather_s, ctx->comp_done[k], 0));
@@ -358,6 +361,7 @@ dlo_status check_ctx(dlo_ctx* ctx) {
 
 dlo_status sync_ctx(dlo_ctx* ctx) {
   DLO_HIP(ctx, hipStreamSynchronize(ctx->copy_s));
+  DLO_HIP(ctx, hipStreamSynchronize(ctx->copy_s2));
   DLO_HIP(ctx, hipStreamSynchronize(ctx->gather_s));
   DLO_HIP(ctx, hipEventSynchronize(ctx->comp_done[0]));
   DLO_HIP(ctx, hipEventSynchronize(ctx->comp_done[1]));
@@ -378,6 +382,7 @@ void free_ctx(dlo_ctx* ctx) {
     }
   }
   if (ctx->own_copy && ctx->copy_s) (void)hipStreamDestroy(ctx->copy_s);
+  if (ctx->copy_s2) (void)hipStreamDestroy(ctx->copy_s2);
   if (ctx->own_gather && ctx->gather_s) (void)hipStreamDestroy(ctx->gather_s);
   delete ctx;
 }
@@ -471,6 +476,7 @@ extern "C" DLO_API dlo_status dlo_create(const dlo_config* cfg, dlo_ctx** out) {
     DLO_HIP(nullptr, hipStreamCreateWithFlags(&c->copy_s, hipStreamNonBlocking));
     c->own_copy = true;
   }
+  DLO_HIP(nullptr, hipStreamCreateWithFlags(&c->copy_s2, hipStreamNonBlocking));
   if (cfg->gather_stream) {
     c->gather_s = cfg->gather_stream;
   } else {
@@ -515,6 +521,7 @@ extern "C" DLO_API dlo_status dlo_load_shards(dlo_ctx* ctx, int32_t block, const
   if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
   // no in-flight copy may read the shards being replaced
   DLO_HIP(ctx, hipStreamSynchronize(ctx->copy_s));
+  DLO_HIP(ctx, hipStreamSynchronize(ctx->copy_s2));
   const int64_t S = b.shard;
   if (b.shards.empty()) {
     b.shards.assign(ctx->dp, nullptr);
@@ -601,6 +608,7 @@ extern "C" DLO_API dlo_status dlo_destroy(dlo_ctx* ctx) {
     DeviceGuard dg(ctx->device);
     if (!ctx->poisoned) {
       (void)hipStreamSynchronize(ctx->copy_s);
+      (void)hipStreamSynchronize(ctx->copy_s2);
       (void)hipStreamSynchronize(ctx->gather_s);
       (void)hipEventSynchronize(ctx->comp_done[0]);
       (void)hipEventSynchronize(ctx->comp_done[1]);
@@ -702,13 +710,27 @@ dlo_status collect_trace(dlo_ctx* ctx, std::vector<dlo_interval>& out, dlo_stats
   }
   if (s) {
     s->last_forward_ms = t_end;
-    double h = 0, a = 0, c = 0;
-    for (auto& iv : out) {
-      const double dur = iv.end_ms - iv.start_ms;
-      if (iv.kind == DLO_IV_H2D) h += dur;
-      if (iv.kind == DLO_IV_ASM) a += dur;
-      if (iv.kind == DLO_IV_COMPUTE) c += dur;
-    }
+    // busy time per stream kind: length of the union of its intervals (the
+    // two copy engines overlap)
+    auto busy = [&](int kind) {
+      std::vector<std::pair<double, double>> v;
+      for (auto& iv : out)
+        if (iv.kind == kind) v.push_back({iv.start_ms, iv.end_ms});
+      std::sort(v.begin(), v.end());
+      double tot = 0, cs = -1e300, ce = -1e300;
+      for (auto& p : v) {
+        if (p.first > ce) {
+          if (ce > cs) tot += ce - cs;
+          cs = p.first;
+          ce = p.second;
+        } else {
+          ce = std::max(ce, p.second);
+        }
+      }
+      if (ce > cs) tot += ce - cs;
+      return tot;
+    };
+    const double h = busy(DLO_IV_H2D), a = busy(DLO_IV_ASM), c = busy(DLO_IV_COMPUTE);
     s->sum_h2d_ms = h;
     s->sum_asm_ms = a;
     s->sum_compute_ms = c;
