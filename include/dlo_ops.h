@@ -47,11 +47,14 @@ DLO_API dlo_status dlo_op_ln_modulate(const float* xin, int32_t d_in, float* xou
 
 /* GEMM on MFMA: acc[i][j] = sum_k a[i][k] * w[j][k] (bf16 operands, fp32
  * accumulation) for i in [0, M), j in [0, N); rows of w at or past w_rows are
- * read as row w_rows - 1 (so padded output columns stay finite).  Epilogues:
- *   DLO_EPI_BIAS_BF16      out bf16 [M][ldo]:  out = acc + bias[j]
- *   DLO_EPI_BIAS_GELU_BF16 out bf16 [M][ldo]:  out = gelu_tanh(acc + bias[j])
- *   DLO_EPI_GATED_F32      out fp32 [M][ldo]:  out += gate[j] * (acc + bias[j])
- *   DLO_EPI_ROWBIAS_BF16   out bf16 [M][ldo]:  out = acc + bias[i]
+ * read as row w_rows - 1 (so padded output columns stay finite).  Epilogues
+ * (bf16 results rounded to nearest even):
+ *   DLO_EPI_BIAS_BF16      out bf16 [M][ldo]:  out[i][j] = acc + bias[j]
+ *   DLO_EPI_BIAS_GELU_BF16 out bf16 [M][ldo]:  out[i][j] = gelu_tanh(acc + bias[j])
+ *   DLO_EPI_GATED_F32      out fp32 [M][ldo]:  out[i][j] += gate[j] * (acc + bias[j])
+ *   DLO_EPI_ROWBIAS_BF16   out bf16 [M][ldo]:  out[i][p(j)] = acc + bias[i]
+ * where p(j) swaps bits 2 and 3 of j (the transposed v layout attention
+ * reads, see dlo_op_attention); this epilogue needs N to be a multiple of 16.
  * bias is bf16, gate fp32.  K must be a multiple of 64; lda, ldw multiples of
  * 8; M, N >= 1; 1 <= w_rows <= N. */
 #define DLO_EPI_BIAS_BF16 0
@@ -68,8 +71,11 @@ DLO_API dlo_status dlo_op_gemm(int32_t epilogue, const uint16_t* a, int32_t lda,
  * with p = softmax_s(q[t] . k[s] / sqrt(hd)), fp32 softmax and accumulation.
  * q[t][c] = qk[t*ld_qk + c] and k[t][c] = qk[t*ld_qk + heads*hd + c]
  * (the q and k thirds of the QKV projection, row-major); v is given
- * transposed: v[s][c] = vt[c*ld_vt + s], with ld_vt >= tokens rounded up to
- * 64 and columns [tokens, ld_vt) finite.  hd = head_dim in {64, 128}. */
+ * transposed with its keys permuted inside every aligned group of 16:
+ * v[s][c] = vt[c*ld_vt + p(s)], p(s) = s with bits 2 and 3 swapped (so the
+ * eight keys one lane multiplies are one aligned 16-byte run); ld_vt >=
+ * tokens rounded up to 64, a multiple of 64, and the columns that hold keys
+ * >= tokens finite.  hd = head_dim in {64, 128}. */
 DLO_API dlo_status dlo_op_attention(const uint16_t* qk, int32_t ld_qk, const uint16_t* vt,
                                     int32_t ld_vt, uint16_t* o, int32_t ld_o, int32_t tokens,
                                     int32_t heads, int32_t head_dim, hipStream_t stream);

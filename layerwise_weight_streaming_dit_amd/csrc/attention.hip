@@ -14,16 +14,24 @@
 // The output is accumulated transposed too, O^T += V^T P^T: P (bf16) is the B
 // operand straight from the S^T registers, and V^T is the A operand.  In the
 // S^T layout, lane group g = l / 32 holds key offsets {8a + 4g + b} (a in
-// {0,1}, b in 0..3) of each 16-key group, so V^T is staged in LDS with the
-// keys of every 16-key group permuted by swapping bits 2 and 3 of the key
-// offset; then each lane's 8 keys are one aligned 16-byte LDS read.  V arrives
-// already transposed from the v projection (v^T = Wv h^T), so staging is
-// plain 16-byte copies split into two 8-byte LDS stores.
+// {0,1}, b in 0..3) of each 16-key group; the v projection writes V^T with
+// bits 2 and 3 of every key offset swapped (vt_key_position), so each lane's
+// 8 keys are one aligned 16-byte run and staging is a plain copy.
+//
+// Softmax work per score: one max, one FMA (scale and max folded), one exp2,
+// one add, half a v_cvt_pk_bf16_f32.  The output is rescaled only when a
+// query's max grows by more than 2^8 over the reference it uses (a
+// wave-uniform branch, usually taken on the first tile only): the
+// probabilities are then at most 256 -- exact in fp32 and in range for bf16 --
+// and the final division by the running sum is unchanged, so the result is
+// the same softmax.  Key masking runs only in the last, partial tile.
 //
 // Tiles: 128 queries (4 waves) per workgroup, 64 keys per step, K and V^T
 // double-buffered in LDS with XOR-swizzled 16-byte chunks; the next tile's
 // global loads are issued before the current tile's MFMAs.
 #include <math.h>
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -33,11 +41,12 @@ namespace dlo {
 namespace {
 
 constexpr int kAttnThreads = 256;
-constexpr int kBQ = 128;  // queries per workgroup (32 per wave)
-constexpr int kBKV = 64;  // keys per step
+constexpr int kBQ = 128;           // queries per workgroup (32 per wave)
+constexpr int kBKV = 64;           // keys per step
+constexpr float kRescaleSlack = 8.0f;  // log2 of the largest unnormalised probability
 
 template <int HD>
-__global__ __launch_bounds__(kAttnThreads) void attention_kernel(
+__global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(
     const uint16_t* __restrict__ qk, int ld_qk, const uint16_t* __restrict__ vt, int ld_vt,
     uint16_t* __restrict__ o, int ld_o, int T, int H, float scale_log2) {
   constexpr int KCH = HD / 8;           // 16-byte chunks per K row
@@ -52,6 +61,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5;
+  const int kc = lane & 31;
   const int h = blockIdx.y;
   const int q0 = blockIdx.x * kBQ + wave * 32;
   const int64_t kcol = static_cast<int64_t>(H) * HD + static_cast<int64_t>(h) * HD;
@@ -59,40 +69,35 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(
   // Q fragments (B operand of S^T = K Q^T).
   bf16x8_t qf[NKK];
   {
-    const int qrow = min(q0 + (lane & 31), T - 1);
+    const int qrow = min(q0 + kc, T - 1);
     const uint16_t* qp = qk + static_cast<int64_t>(qrow) * ld_qk + static_cast<int64_t>(h) * HD + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qp + kk * 16);
   }
 
   // Staging addresses.
-  int k_row[NK], k_lds[NK], v_lds0[NV], v_lds1[NV];
+  int k_row[NK], k_chunk[NK], k_lds[NK], v_lds[NV];
   const uint16_t* v_src[NV];
 #pragma unroll
   for (int i = 0; i < NK; ++i) {
     const int q = tid + i * kAttnThreads, j = q / KCH, c = q % KCH;
     k_row[i] = j;
+    k_chunk[i] = c;
     k_lds[i] = j * HD + ((c ^ (j & KSWZ)) << 3);
   }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int q = tid + i * kAttnThreads, row = q >> 3, c = q & 7;
     v_src[i] = vt + (static_cast<int64_t>(h) * HD + row) * ld_vt + c * 8;
-    // keys 8c..8c+3 -> group position 4(c&1); keys 8c+4..8c+7 -> 8 + 4(c&1)
-    const int grp = c >> 1, half = 4 * (c & 1);
-    const int p0 = 16 * grp + half, p1 = 16 * grp + 8 + half;
-    v_lds0[i] = row * kBKV + ((((p0 >> 3) ^ (row & 7))) << 3) + (p0 & 7);
-    v_lds1[i] = row * kBKV + ((((p1 >> 3) ^ (row & 7))) << 3) + (p1 & 7);
+    v_lds[i] = row * kBKV + ((c ^ (row & 7)) << 3);
   }
-  const int kc = (lane & 31);
 
   u32x4_t rk[NK], rv[NV];
   auto load_tile = [&](int key0) {
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
-      const int q = tid + i * kAttnThreads, c = q % KCH;
       const int key = min(key0 + k_row[i], T - 1);
-      rk[i] = *reinterpret_cast<const u32x4_t*>(qk + static_cast<int64_t>(key) * ld_qk + kcol + c * 8);
+      rk[i] = *reinterpret_cast<const u32x4_t*>(qk + static_cast<int64_t>(key) * ld_qk + kcol + k_chunk[i] * 8);
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) rv[i] = *reinterpret_cast<const u32x4_t*>(v_src[i] + key0);
@@ -101,10 +106,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(
 #pragma unroll
     for (int i = 0; i < NK; ++i) *reinterpret_cast<u32x4_t*>(&sK[buf][k_lds[i]]) = rk[i];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      *reinterpret_cast<u32x2_t*>(&sV[buf][v_lds0[i]]) = u32x2_t{rv[i].x, rv[i].y};
-      *reinterpret_cast<u32x2_t*>(&sV[buf][v_lds1[i]]) = u32x2_t{rv[i].z, rv[i].w};
-    }
+    for (int i = 0; i < NV; ++i) *reinterpret_cast<u32x4_t*>(&sV[buf][v_lds[i]]) = rv[i];
   };
 
   f32x16_t oacc[NIB];
@@ -112,18 +114,11 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(
   for (int ib = 0; ib < NIB; ++ib)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[ib][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_use = -INFINITY;  // reference max (scaled, base 2) the probabilities use
+  float l_run = 0.f;        // this lane's half of the running sum
 
-  const int ntiles = (T + kBKV - 1) / kBKV;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile((t + 1) * kBKV);
-
+  auto process = [&](auto mask_tag, int t, int cur) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     // ---- scores S^T for two 32-key blocks
     f32x16_t s[2];
 #pragma unroll
@@ -138,33 +133,31 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
       }
     }
-
-    // ---- online softmax (base 2; scale folded into scale_log2)
-    const int key_base = t * kBKV;
-    const bool tail = key_base + kBKV > T;
+    // ---- max over raw scores (the scale is positive)
     float mloc = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float v = s[kb][r] * scale_log2;
-        if (tail) {
-          const int key = key_base + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= T) v = -INFINITY;
+        if constexpr (MASK) {
+          const int key = t * kBKV + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key >= T) s[kb][r] = -INFINITY;
         }
-        s[kb][r] = v;
-        mloc = fmaxf(mloc, v);
+        mloc = fmaxf(mloc, s[kb][r]);
       }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+    const float mc = mloc * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mc > m_use + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_use, mc);
+      const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int ib = 0; ib < NIB; ++ib)
+      for (int ib = 0; ib < NIB; ++ib)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[ib][r] *= alpha;
-
+        for (int r = 0; r < 16; ++r) oacc[ib][r] *= alpha;
+      m_use = m_new;
+    }
+    const float nm = -m_use;
     bf16x8_t pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -173,14 +166,13 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(
         u32x4_t w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(s[kb][8 * ks + 2 * e] - m_new);
-          const float p1 = __builtin_amdgcn_exp2f(s[kb][8 * ks + 2 * e + 1] - m_new);
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * ks + 2 * e], scale_log2, nm));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * ks + 2 * e + 1], scale_log2, nm));
           l_run += p0 + p1;
           w[e] = pack_bf16x2(p0, p1);
         }
         pb[kb][ks] = __builtin_bit_cast(bf16x8_t, w);
       }
-
     // ---- O^T += V^T P^T
 #pragma unroll
     for (int ib = 0; ib < NIB; ++ib) {
@@ -194,10 +186,26 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(
           oacc[ib] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][ks], oacc[ib], 0, 0, 0);
         }
     }
+  };
 
-    if (more) store_tile(cur ^ 1);
+  const int ntiles = (T + kBKV - 1) / kBKV;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  // every tile but the last: no key masking
+  for (int t = 0; t + 1 < ntiles; ++t) {
+    const int cur = t & 1;
+    load_tile((t + 1) * kBKV);
+    process(std::false_type{}, t, cur);
+    store_tile(cur ^ 1);
     __syncthreads();
   }
+  // the last tile, masked only if it is partial
+  if (T % kBKV != 0)
+    process(std::true_type{}, ntiles - 1, (ntiles - 1) & 1);
+  else
+    process(std::false_type{}, ntiles - 1, (ntiles - 1) & 1);
 
   // ---- normalise and store: lane holds query q0 + l%32, head dims
   // ib*32 + 8*rg + 4*g + 0..3 for rg = 0..3 (four consecutive -> 8 bytes).

@@ -17,17 +17,26 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16 bit pattern, round to nearest even; NaN stays NaN (quiet).
+// fp32 -> bf16 bit pattern, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-// Two fp32 -> packed pair of bf16 (lo in bits 0..15).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed pair of bf16 (lo in bits 0..15), round to nearest even,
+// with gfx950's v_cvt_pk_bf16_f32 (one instruction per pair).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const bf16x2_t v = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Column position of token j in the transposed v buffer: inside every aligned
+// group of 16 tokens, bits 2 and 3 of the offset are swapped, so that the
+// 8 keys each lane of attention's P.V step needs are one aligned 16-byte run.
+__device__ __forceinline__ int vt_key_position(int j) {
+  return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
 }
 
 // tanh-approximated GELU: 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))),

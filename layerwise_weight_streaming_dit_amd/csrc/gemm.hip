@@ -22,7 +22,8 @@
 //   x += gate * (acc + bias) in fp32 (attention output and MLP down, the
 //   gated residual of adaLN-Zero), and per-row bias -> bf16 (the v projection
 //   computed transposed, v^T = Wv h^T, which is the operand layout attention
-//   needs for P V).
+//   needs for P V; each output column goes to its permuted key position, see
+//   vt_key_position).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -175,7 +176,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
           float* x = static_cast<float*>(g.out);
           x[o] = x[o] + cgate * (v + cbias);
         } else {
-          static_cast<uint16_t*>(g.out)[o] = f32_to_bf16(v + bf16_to_f32(g.bias[row]));
+          // transposed v: token `col` lands at its permuted key position
+          const int64_t ot = static_cast<int64_t>(row) * g.ldo + vt_key_position(col);
+          static_cast<uint16_t*>(g.out)[ot] = f32_to_bf16(v + bf16_to_f32(g.bias[row]));
         }
       }
     }

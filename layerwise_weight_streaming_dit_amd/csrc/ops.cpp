@@ -67,6 +67,8 @@ extern "C" DLO_API dlo_status dlo_op_gemm(int32_t epilogue, const uint16_t* a, i
   if (w_rows < 1 || w_rows > N) return fail(DLO_E_SHAPE, "w_rows %d outside [1, N=%d]", w_rows, N);
   if (lda < K || ldw < K || lda % 8 || ldw % 8) return fail(DLO_E_SHAPE, "lda %d / ldw %d must be >= K and multiples of 8", lda, ldw);
   if (ldo < N) return fail(DLO_E_SHAPE, "ldo %d < N %d", ldo, N);
+  if (epilogue == DLO_EPI_ROWBIAS_BF16 && N % 16 != 0)
+    return fail(DLO_E_SHAPE, "the transposed-v epilogue needs N (%d) to be a multiple of 16", N);
   if (!aligned(a, 16) || !aligned(w, 16)) return fail(DLO_E_INVAL, "operands must be 16-byte aligned");
   GemmArgs g{a, w, bias, gate, out, lda, ldw, ldo, M, N, K, w_rows};
   return launched(launch_gemm(epilogue, g, s), "gemm");
@@ -83,7 +85,7 @@ extern "C" DLO_API dlo_status dlo_op_attention(const uint16_t* qk, int32_t ld_qk
   if (ld_qk < 2 * d || ld_qk % 8) return fail(DLO_E_SHAPE, "ld_qk %d must be >= 2*d and a multiple of 8", ld_qk);
   if (ld_o < d || ld_o % 4) return fail(DLO_E_SHAPE, "ld_o %d must be >= d and a multiple of 4", ld_o);
   const int64_t tp = (int64_t(tokens) + 63) / 64 * 64;
-  if (ld_vt < tp || ld_vt % 8) return fail(DLO_E_SHAPE, "ld_vt %d must be >= %lld and a multiple of 8", ld_vt, (long long)tp);
+  if (ld_vt < tp || ld_vt % 64) return fail(DLO_E_SHAPE, "ld_vt %d must be >= %lld and a multiple of 64", ld_vt, (long long)tp);
   if (!aligned(qk, 16) || !aligned(vt, 16) || !aligned(o, 8)) return fail(DLO_E_INVAL, "misaligned pointer");
   return launched(launch_attention(qk, ld_qk, vt, ld_vt, o, ld_o, tokens, heads, head_dim, s), "attention");
 }

@@ -16,6 +16,13 @@ def _bf16(a):
     return synth.bf16_bits_from_f32(np.asarray(a, np.float32))
 
 
+def vt_position(j):
+    """Documented layout of the transposed v buffer (include/dlo_ops.h):
+    token j sits at column j with bits 2 and 3 swapped."""
+    j = np.asarray(j)
+    return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1)
+
+
 # ------------------------------------------------------------- reconstruction
 
 @pytest.mark.parametrize("n", [1, 7, 8, 9, 4095, 65536 + 13, (1 << 21) + 5])
@@ -97,7 +104,8 @@ def _gemm_case(epi, M, N, K, w_rows=None, seed=0):
         return bf16_to_f64(host(out, np.uint16)), D.gelu_tanh(acc + bf)
     if epi == dlo.EPI_GATED_F32:
         return host(out).astype(np.float64), x0 + gate.astype(np.float64) * (acc + bf)
-    return bf16_to_f64(host(out, np.uint16)), acc + bf[:, None]
+    got = bf16_to_f64(host(out, np.uint16))
+    return got[:, vt_position(np.arange(N))], acc + bf[:, None]
 
 
 @pytest.mark.parametrize("epi", [dlo.EPI_BIAS_BF16, dlo.EPI_BIAS_GELU_BF16, dlo.EPI_GATED_F32, dlo.EPI_ROWBIAS_BF16])
@@ -114,6 +122,31 @@ def test_gemm_clamped_w_rows():
     got, want = _gemm_case(dlo.EPI_ROWBIAS_BF16, 512, 1088, 256, w_rows=1000, seed=5)
     ok, ma, mr = within(got, want, rtol=1e-2, atol=1e-2)
     assert ok, (ma, mr)
+
+
+def test_gemm_epilogue_rounding_is_rne_exact():
+    """A one-hot A makes acc = w[j][i] exactly; with bias of similar
+    magnitude acc + bias is exact in fp32, so the bf16 output must be the
+    round-to-nearest-even of that sum, bit for bit (ties included)."""
+    rng = np.random.default_rng(77)
+    M, N, K = 128, 256, 128
+    a = np.zeros((M, K), np.float32)
+    a[np.arange(M), np.arange(M) % K] = 1.0
+    # w and bias: bf16 values whose fp32 sum has bits below bf16 precision,
+    # including exact ties (lowest 16 bits 0x8000)
+    w = _bf16((rng.integers(-256, 256, size=(N, K)) / 64.0).astype(np.float32))
+    # bias: +-(1 + m/128) * 2^e, e in [-8, -5] -- exact bf16, so every fp32
+    # sum w + bias spans at most 17 significant bits (exact)
+    mant = 1.0 + rng.integers(0, 128, size=N) / 128.0
+    bias = _bf16((rng.choice([-1.0, 1.0], size=N) * mant * 2.0 ** rng.integers(-8, -4, size=N)).astype(np.float32))
+    t = torch()
+    out = t.empty((M, N), dtype=t.int16, device="cuda")
+    dlo.op_gemm(dlo.EPI_BIAS_BF16, dev(_bf16(a)), K, dev(w), K, N, dev(bias), None, out, N, M, N, K)
+    acc = bf16_to_f64(w)[:, np.arange(M) % K].T.astype(np.float32)
+    exact = acc + bf16_to_f64(bias).astype(np.float32)[None, :]
+    assert np.all(exact.astype(np.float64) == bf16_to_f64(w)[:, np.arange(M) % K].T + bf16_to_f64(bias)[None, :])
+    want = synth.bf16_bits_from_f32(exact)
+    assert np.array_equal(host(out, np.uint16), want)
 
 
 def test_gemm_large_tile_shapes():
@@ -134,7 +167,7 @@ def _attention_case(T, H, hd, qscale=1.0, seed=0):
     v = _bf16(rng.standard_normal((T, d)))
     tp = (T + 63) // 64 * 64
     vt = np.zeros((d, tp), np.uint16)
-    vt[:, :T] = v.T
+    vt[:, vt_position(np.arange(T))] = v.T
     qk = np.concatenate([q, k], axis=1)
     t = torch()
     o = t.empty((T, d), dtype=t.int16, device="cuda")
