@@ -54,9 +54,11 @@ DLO_API dlo_status dlo_op_ln_modulate(const float* xin, int32_t d_in, float* xou
  *   DLO_EPI_GATED_F32      out fp32 [M][ldo]:  out[i][j] += gate[j] * (acc + bias[j])
  *   DLO_EPI_ROWBIAS_BF16   out bf16 [M][ldo]:  out[i][p(j)] = acc + bias[i]
  * where p(j) swaps bits 2 and 3 of j (the transposed v layout attention
- * reads, see dlo_op_attention); this epilogue needs N to be a multiple of 16.
- * bias is bf16, gate fp32.  K must be a multiple of 64; lda, ldw multiples of
- * 8; M, N >= 1; 1 <= w_rows <= N. */
+ * reads, see dlo_op_attention).  bias is bf16, gate fp32.  M >= 1; N a
+ * multiple of 16; K a multiple of 128; lda, ldw multiples of 8 and >= K;
+ * ldo a multiple of 4 and >= N; 1 <= w_rows <= N; a, w 16-byte aligned, out
+ * 8-byte (16 for the fp32 epilogue), bias 8-byte (column bias), gate
+ * 16-byte. */
 #define DLO_EPI_BIAS_BF16 0
 #define DLO_EPI_BIAS_GELU_BF16 1
 #define DLO_EPI_GATED_F32 2

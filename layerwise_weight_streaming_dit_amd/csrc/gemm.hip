@@ -8,10 +8,16 @@
 //
 // A workgroup computes a BM x BN tile with WM x WN waves; each wave owns a
 // (BM / WM) x (BN / WN) sub-tile made of 32x32 MFMA tiles.  K advances in
-// steps of 64: each step's A and W tiles are staged in LDS (double-buffered,
-// one barrier per step) with 16-byte chunks XOR-swizzled by row, so the
-// 16-byte fragment reads of 8 consecutive rows hit distinct banks.  The next
-// step's global loads are issued before the current step's MFMAs.
+// steps of 32 through a ring of four LDS stages.  Global data moves straight
+// into LDS with gfx950's global_load_lds_dwordx4 (no staging registers), three
+// steps ahead of the MFMAs that consume it, so HBM/L2 latency hides behind
+// three steps of MFMA work; one barrier per step both publishes a landed stage
+// and frees the stage read one step earlier for the next load.  Each wave
+// writes 1 KB of LDS per load instruction (64 lanes x 16 bytes, contiguous), so
+// the row/chunk swizzle is applied on the global side: LDS slot s holds row
+// s / 4, 16-byte chunk (s % 4) ^ f(row), f(row) = ((row >> 1) ^ (row >> 2)) & 3,
+// which keeps the fragment reads of 8 (or 16) consecutive rows on distinct
+// banks.
 //
 // Workgroups are dispatched round-robin over the 8 XCDs; the tile order gives
 // each XCD a contiguous range of tiles, walked in groups of kGroupM tile rows,
@@ -24,6 +30,8 @@
 //   computed transposed, v^T = Wv h^T, which is the operand layout attention
 //   needs for P V; each output column goes to its permuted key position, see
 //   vt_key_position).
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -31,19 +39,47 @@ namespace dlo {
 
 namespace {
 
-constexpr int kBK = 64;
+// 16 bytes per lane from global memory straight into LDS: lane i's data lands
+// at lds + 16 * i (global_load_lds_dwordx4).  The LDS address-space cast only
+// exists in the device pass; the host pass sees an empty body.
+__device__ __forceinline__ void dma16(const uint16_t* gsrc, uint16_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#endif
+}
+
+constexpr int kBK = 32;      // K per stage
 constexpr int kGroupM = 8;
+
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+
+// s_waitcnt vmcnt(n) leaving lgkmcnt / expcnt unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int V>
+using IC = std::integral_constant<int, V>;
 
 template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
-  constexpr int THREADS = WM * WN * 64;
+  constexpr int W = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int LA = BM * 8 / THREADS, LB = BN * 8 / THREADS;
-  static_assert(LA * THREADS == BM * 8 && LB * THREADS == BN * 8, "tile/threads mismatch");
+  constexpr int STAGE_A = BM * kBK, STAGE_B = BN * kBK;  // elements per stage
+  constexpr int LA = BM / 16 / W, LB = BN / 16 / W;      // 1 KB DMA loads per wave per stage
+  static_assert(LA * 16 * W == BM && LB * 16 * W == BN, "tile/waves mismatch");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smA[2][BM * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t smB[2][BN * kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[STAGE_A];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA1[STAGE_A];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA2[STAGE_A];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA3[STAGE_A];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[STAGE_B];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB1[STAGE_B];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB2[STAGE_B];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB3[STAGE_B];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -64,33 +100,48 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
   const int tile_n = in_group / gsz;
   const int m0 = tile_m * BM, n0 = tile_n * BN;
 
-  // ---- global -> register staging addresses (clamped rows keep loads in bounds)
-  const uint16_t* pa[LA];
-  const uint16_t* pb[LB];
-  int la_off[LA], lb_off[LB];
+  // ---- per-lane global sources of the DMA loads (rows clamped in bounds)
+  const uint16_t* ga[LA];
+  const uint16_t* gb[LB];
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
-    const int q = tid + i * THREADS, row = q >> 3, c = q & 7;
-    const int gr = min(m0 + row, g.M - 1);
-    pa[i] = g.a + static_cast<int64_t>(gr) * g.lda + c * 8;
-    la_off[i] = row * kBK + ((c ^ (row & 7)) << 3);
+    const int slot = (wave * LA + i) * 64 + lane, row = slot >> 2;
+    const int c = (slot & 3) ^ swz(row);
+    ga[i] = g.a + static_cast<int64_t>(min(m0 + row, g.M - 1)) * g.lda + c * 8;
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
-    const int q = tid + i * THREADS, row = q >> 3, c = q & 7;
-    const int gr = min(n0 + row, g.w_rows - 1);
-    pb[i] = g.w + static_cast<int64_t>(gr) * g.ldw + c * 8;
-    lb_off[i] = row * kBK + ((c ^ (row & 7)) << 3);
+    const int slot = (wave * LB + i) * 64 + lane, row = slot >> 2;
+    const int c = (slot & 3) ^ swz(row);
+    gb[i] = g.w + static_cast<int64_t>(min(n0 + row, g.w_rows - 1)) * g.ldw + c * 8;
   }
+  const int nk = g.K / kBK;
 
-  // ---- fragment read offsets (elements) for k-substep 0; substep ks adds
-  // chunk 2*ks, applied through the same XOR.
-  int fa_row[TM], fb_row[TN];
+  auto stageA = [&](auto S) -> uint16_t* {
+    if constexpr (decltype(S)::value == 0) return sA0;
+    else if constexpr (decltype(S)::value == 1) return sA1;
+    else if constexpr (decltype(S)::value == 2) return sA2;
+    else return sA3;
+  };
+  auto stageB = [&](auto S) -> uint16_t* {
+    if constexpr (decltype(S)::value == 0) return sB0;
+    else if constexpr (decltype(S)::value == 1) return sB1;
+    else if constexpr (decltype(S)::value == 2) return sB2;
+    else return sB3;
+  };
+  // Issue the DMA loads of K step `kstep` (clamped to the last step, so the
+  // count of loads in flight is the same on every step) into stage S.
+  auto issue = [&](auto S, int kstep) {
+    const int koff = min(kstep, nk - 1) * kBK;
+    uint16_t* a = stageA(S);
+    uint16_t* b = stageB(S);
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) fa_row[tm] = wm * WTM + tm * 32 + (lane & 31);
+    for (int i = 0; i < LA; ++i)
+      dma16(ga[i] + koff, a + (wave * LA + i) * 512);
 #pragma unroll
-  for (int tn = 0; tn < TN; ++tn) fb_row[tn] = wn * WTN + tn * 32 + (lane & 31);
-  const int fchunk = lane >> 5;
+    for (int i = 0; i < LB; ++i)
+      dma16(gb[i] + koff, b + (wave * LB + i) * 512);
+  };
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -100,85 +151,105 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
 
-  u32x4_t ra[LA], rb[LB];
-  const int nk = g.K / kBK;
-
-#pragma unroll
-  for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(pa[i]);
-#pragma unroll
-  for (int i = 0; i < LB; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(pb[i]);
-#pragma unroll
-  for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4_t*>(&smA[0][la_off[i]]) = ra[i];
-#pragma unroll
-  for (int i = 0; i < LB; ++i) *reinterpret_cast<u32x4_t*>(&smB[0][lb_off[i]]) = rb[i];
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int koff = (kt + 1) * kBK;
-#pragma unroll
-      for (int i = 0; i < LA; ++i) ra[i] = *reinterpret_cast<const u32x4_t*>(pa[i] + koff);
-#pragma unroll
-      for (int i = 0; i < LB; ++i) rb[i] = *reinterpret_cast<const u32x4_t*>(pb[i] + koff);
-    }
+  auto compute = [&](auto S) {
+    const uint16_t* a = stageA(S);
+    const uint16_t* b = stageB(S);
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int c = ks * 2 + (lane >> 5);
       bf16x8_t fa[TM], fb[TN];
-      const int c = ks * 2 + fchunk;
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) {
-        const int row = fa_row[tm];
-        fa[tm] = *reinterpret_cast<const bf16x8_t*>(&smA[cur][row * kBK + ((c ^ (row & 7)) << 3)]);
+        const int row = wm * WTM + tm * 32 + (lane & 31);
+        fa[tm] = *reinterpret_cast<const bf16x8_t*>(a + row * kBK + ((c ^ swz(row)) << 3));
       }
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) {
-        const int row = fb_row[tn];
-        fb[tn] = *reinterpret_cast<const bf16x8_t*>(&smB[cur][row * kBK + ((c ^ (row & 7)) << 3)]);
+        const int row = wn * WTN + tn * 32 + (lane & 31);
+        fb[tn] = *reinterpret_cast<const bf16x8_t*>(b + row * kBK + ((c ^ swz(row)) << 3));
       }
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[tm], fb[tn], acc[tm][tn], 0, 0, 0);
+          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[tn], fa[tm], acc[tm][tn], 0, 0, 0);
     }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < LA; ++i) *reinterpret_cast<u32x4_t*>(&smA[cur ^ 1][la_off[i]]) = ra[i];
-#pragma unroll
-      for (int i = 0; i < LB; ++i) *reinterpret_cast<u32x4_t*>(&smB[cur ^ 1][lb_off[i]]) = rb[i];
-    }
-    __syncthreads();
-  }
+  };
+  // One K step on stage S: wait for this wave's loads of the step (two later
+  // steps' loads may stay in flight), barrier (everyone's loads landed, and
+  // everyone finished the previous step, whose stage is reloaded now), then
+  // MFMAs.
+  auto step = [&](auto S, int kt) {
+    wait_vmcnt<2 * (LA + LB)>();
+    __builtin_amdgcn_s_barrier();
+    issue(IC<(decltype(S)::value + 3) % 4>{}, kt + 3);
+    compute(S);
+  };
 
-  // ---- epilogue
+  issue(IC<0>{}, 0);
+  issue(IC<1>{}, 1);
+  issue(IC<2>{}, 2);
+  // K is a multiple of 4 steps (128), so the ring unrolls without early exits
+  for (int kt = 0; kt < nk; kt += 4) {
+    step(IC<0>{}, kt);
+    step(IC<1>{}, kt + 1);
+    step(IC<2>{}, kt + 2);
+    step(IC<3>{}, kt + 3);
+  }
+  wait_vmcnt<0>();  // drain the clamped tail loads before the epilogue
+
+  // ---- epilogue.  The MFMAs above take W as their first operand, so each
+  // 32x32 accumulator is a tile of C^T: lane l owns output row (l % 32) of the
+  // tile and, for q = 0..3, the four consecutive output columns
+  // 8q + 4(l / 32) + 0..3 (registers 4q..4q+3) -- one 8-byte bf16 store or
+  // one 16-byte fp32 load/store each.  N is a multiple of 16.
 #pragma unroll
-  for (int tn = 0; tn < TN; ++tn) {
-    const int col = n0 + wn * WTN + tn * 32 + (lane & 31);
-    if (col >= g.N) continue;
-    float cbias = 0.f, cgate = 0.f;
-    if constexpr (EPI != EPI_ROWBIAS_BF16) cbias = bf16_to_f32(g.bias[col]);
-    if constexpr (EPI == EPI_GATED_F32) cgate = g.gate[col];
+  for (int tm = 0; tm < TM; ++tm) {
+    const int row = m0 + wm * WTM + tm * 32 + (lane & 31);
+    if (row >= g.M) continue;
+    const int64_t orow = static_cast<int64_t>(row) * g.ldo;
+    float rbias = 0.f;
+    if constexpr (EPI == EPI_ROWBIAS_BF16) rbias = bf16_to_f32(g.bias[row]);
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
+    for (int tn = 0; tn < TN; ++tn) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * WTM + tm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row >= g.M) continue;
-        const float v = acc[tm][tn][r];
-        const int64_t o = static_cast<int64_t>(row) * g.ldo + col;
-        if constexpr (EPI == EPI_BIAS_BF16) {
-          static_cast<uint16_t*>(g.out)[o] = f32_to_bf16(v + cbias);
-        } else if constexpr (EPI == EPI_BIAS_GELU_BF16) {
-          static_cast<uint16_t*>(g.out)[o] = f32_to_bf16(gelu_tanh(v + cbias));
-        } else if constexpr (EPI == EPI_GATED_F32) {
-          float* x = static_cast<float*>(g.out);
-          x[o] = x[o] + cgate * (v + cbias);
+      for (int q = 0; q < 4; ++q) {
+        const int col = n0 + wn * WTN + tn * 32 + 8 * q + 4 * (lane >> 5);
+        if (col >= g.N) continue;
+        f32x4_t v;
+        v.x = acc[tm][tn][4 * q];
+        v.y = acc[tm][tn][4 * q + 1];
+        v.z = acc[tm][tn][4 * q + 2];
+        v.w = acc[tm][tn][4 * q + 3];
+        if constexpr (EPI == EPI_ROWBIAS_BF16) {
+          // transposed v: tokens col..col+3 land at their permuted key
+          // positions, which are consecutive (only bits 2 and 3 move)
+          v += rbias;
+          u32x2_t w;
+          w.x = pack_bf16x2(v.x, v.y);
+          w.y = pack_bf16x2(v.z, v.w);
+          *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(g.out) + orow + vt_key_position(col)) = w;
         } else {
-          // transposed v: token `col` lands at its permuted key position
-          const int64_t ot = static_cast<int64_t>(row) * g.ldo + vt_key_position(col);
-          static_cast<uint16_t*>(g.out)[ot] = f32_to_bf16(v + bf16_to_f32(g.bias[row]));
+          const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(g.bias + col);
+          const f32x4_t b = {__uint_as_float(bb.x << 16), __uint_as_float(bb.x & 0xffff0000u),
+                             __uint_as_float(bb.y << 16), __uint_as_float(bb.y & 0xffff0000u)};
+          v += b;
+          if constexpr (EPI == EPI_GATED_F32) {
+            float* x = static_cast<float*>(g.out) + orow + col;
+            const f32x4_t gt = *reinterpret_cast<const f32x4_t*>(g.gate + col);
+            *reinterpret_cast<f32x4_t*>(x) = *reinterpret_cast<const f32x4_t*>(x) + gt * v;
+          } else {
+            if constexpr (EPI == EPI_BIAS_GELU_BF16) {
+              v.x = gelu_tanh(v.x);
+              v.y = gelu_tanh(v.y);
+              v.z = gelu_tanh(v.z);
+              v.w = gelu_tanh(v.w);
+            }
+            u32x2_t w;
+            w.x = pack_bf16x2(v.x, v.y);
+            w.y = pack_bf16x2(v.z, v.w);
+            *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(g.out) + orow + col) = w;
+          }
         }
       }
     }

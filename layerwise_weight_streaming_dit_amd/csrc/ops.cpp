@@ -63,13 +63,16 @@ extern "C" DLO_API dlo_status dlo_op_gemm(int32_t epilogue, const uint16_t* a, i
     return fail(DLO_E_INVAL, "unknown epilogue %d", epilogue);
   if (!a || !w || !bias || !out) return fail(DLO_E_INVAL, "NULL pointer");
   if (epilogue == DLO_EPI_GATED_F32 && !gate) return fail(DLO_E_INVAL, "gate is NULL");
-  if (M < 1 || N < 1 || K < 64 || K % 64 != 0) return fail(DLO_E_SHAPE, "M %d, N %d, K %d (K multiple of 64)", M, N, K);
+  if (M < 1 || N < 16 || N % 16 != 0 || K < 128 || K % 128 != 0)
+    return fail(DLO_E_SHAPE, "M %d, N %d, K %d (N a multiple of 16, K of 128)", M, N, K);
   if (w_rows < 1 || w_rows > N) return fail(DLO_E_SHAPE, "w_rows %d outside [1, N=%d]", w_rows, N);
   if (lda < K || ldw < K || lda % 8 || ldw % 8) return fail(DLO_E_SHAPE, "lda %d / ldw %d must be >= K and multiples of 8", lda, ldw);
-  if (ldo < N) return fail(DLO_E_SHAPE, "ldo %d < N %d", ldo, N);
-  if (epilogue == DLO_EPI_ROWBIAS_BF16 && N % 16 != 0)
-    return fail(DLO_E_SHAPE, "the transposed-v epilogue needs N (%d) to be a multiple of 16", N);
+  if (ldo < N || ldo % 4) return fail(DLO_E_SHAPE, "ldo %d must be >= N %d and a multiple of 4", ldo, N);
   if (!aligned(a, 16) || !aligned(w, 16)) return fail(DLO_E_INVAL, "operands must be 16-byte aligned");
+  const size_t oal = epilogue == DLO_EPI_GATED_F32 ? 16 : 8;
+  if (!aligned(out, oal) || !aligned(bias, epilogue == DLO_EPI_ROWBIAS_BF16 ? 2 : 8) ||
+      (gate && !aligned(gate, 16)))
+    return fail(DLO_E_INVAL, "out, bias or gate misaligned for vector access");
   GemmArgs g{a, w, bias, gate, out, lda, ldw, ldo, M, N, K, w_rows};
   return launched(launch_gemm(epilogue, g, s), "gemm");
 }

@@ -127,8 +127,10 @@ def test_op_validation_without_launch():
     lib = L.lib()
     fake = 4096  # never dereferenced: every call below fails validation first
     assert lib.dlo_op_gemm(0, fake, 64, fake, 64, 64, fake, None, fake, 64, 64, 64, 63, None) == L.E_SHAPE
-    assert lib.dlo_op_gemm(9, fake, 64, fake, 64, 64, fake, None, fake, 64, 64, 64, 64, None) == L.E_INVAL
-    assert lib.dlo_op_gemm(2, fake, 64, fake, 64, 64, fake, None, fake, 64, 64, 64, 64, None) == L.E_INVAL
+    assert lib.dlo_op_gemm(0, fake, 64, fake, 64, 64, fake, None, fake, 64, 64, 64, 64, None) == L.E_SHAPE
+    assert lib.dlo_op_gemm(0, fake, 128, fake, 128, 24, fake, None, fake, 24, 64, 24, 128, None) == L.E_SHAPE
+    assert lib.dlo_op_gemm(9, fake, 128, fake, 128, 64, fake, None, fake, 64, 64, 64, 128, None) == L.E_INVAL
+    assert lib.dlo_op_gemm(2, fake, 128, fake, 128, 64, fake, None, fake, 64, 64, 64, 128, None) == L.E_INVAL
     assert lib.dlo_op_attention(fake, 256, fake, 64, fake, 128, 10, 1, 96, None) == L.E_SHAPE
     assert lib.dlo_op_attention(fake, 256, fake, 32, fake, 128, 40, 1, 128, None) == L.E_SHAPE
     assert lib.dlo_op_adaln(fake, fake, fake, fake, 10, 100, None) == L.E_SHAPE

@@ -110,7 +110,7 @@ def _gemm_case(epi, M, N, K, w_rows=None, seed=0):
 
 @pytest.mark.parametrize("epi", [dlo.EPI_BIAS_BF16, dlo.EPI_BIAS_GELU_BF16, dlo.EPI_GATED_F32, dlo.EPI_ROWBIAS_BF16])
 @pytest.mark.parametrize("M,N,K", [(256, 768, 256), (300, 256, 1024), (1000, 512, 512), (4096 + 17, 2048, 256),
-                                   (33, 128, 64)])
+                                   (33, 128, 128), (1, 16, 128), (700, 1040, 384)])
 def test_gemm(epi, M, N, K):
     got, want = _gemm_case(epi, M, N, K, seed=M + N + K + epi)
     ok, ma, mr = within(got, want, rtol=1e-2, atol=1e-2)
