@@ -8,16 +8,14 @@
 //
 // A workgroup computes a BM x BN tile with WM x WN waves; each wave owns a
 // (BM / WM) x (BN / WN) sub-tile made of 32x32 MFMA tiles.  K advances in
-// steps of 32 through a ring of four LDS stages.  Global data moves straight
-// into LDS with gfx950's global_load_lds_dwordx4 (no staging registers), three
-// steps ahead of the MFMAs that consume it, so HBM/L2 latency hides behind
-// three steps of MFMA work; one barrier per step both publishes a landed stage
-// and frees the stage read one step earlier for the next load.  Each wave
-// writes 1 KB of LDS per load instruction (64 lanes x 16 bytes, contiguous), so
-// the row/chunk swizzle is applied on the global side: LDS slot s holds row
-// s / 4, 16-byte chunk (s % 4) ^ f(row), f(row) = ((row >> 1) ^ (row >> 2)) & 3,
-// which keeps the fragment reads of 8 (or 16) consecutive rows on distinct
-// banks.
+// steps of 64 through two LDS stages.  Global data moves straight into LDS
+// with gfx950's global_load_lds_dwordx4 (no staging registers), one step
+// ahead of the MFMAs that consume it; each row's 64 k values are one full
+// 128-byte cache line, so every line is fetched from L2 once per tile.  One
+// barrier per step both publishes a landed stage and frees the other one.
+// Each wave writes 1 KB of LDS per load instruction (64 lanes x 16 bytes,
+// contiguous), so the row/chunk swizzle is applied on the global side: LDS
+// slot s holds row s / 8, 16-byte chunk (s % 8) ^ swz(row).
 //
 // Workgroups are dispatched round-robin over the 8 XCDs; the tile order gives
 // each XCD a contiguous range of tiles, walked in groups of kGroupM tile rows,
@@ -48,10 +46,12 @@ __device__ __forceinline__ void dma16(const uint16_t* gsrc, uint16_t* lds) {
 #endif
 }
 
-constexpr int kBK = 32;      // K per stage
-constexpr int kGroupM = 8;
+constexpr int kBK = 64;      // K per stage: one full 128-byte line per row
+constexpr int kGroupM = 4;
 
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+// 16-byte chunk swizzle of a 128-byte LDS row: keeps the fragment reads of 8
+// (32 banks) or 16 (64 banks) consecutive rows on distinct banks.
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 // s_waitcnt vmcnt(n) leaving lgkmcnt / expcnt unconstrained (gfx9 encoding).
 template <int N>
@@ -59,6 +59,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+
+// s_waitcnt lgkmcnt(0) leaving vmcnt / expcnt unconstrained.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
 template <int V>
 using IC = std::integral_constant<int, V>;
@@ -69,17 +72,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int STAGE_A = BM * kBK, STAGE_B = BN * kBK;  // elements per stage
-  constexpr int LA = BM / 16 / W, LB = BN / 16 / W;      // 1 KB DMA loads per wave per stage
-  static_assert(LA * 16 * W == BM && LB * 16 * W == BN, "tile/waves mismatch");
+  constexpr int LA = BM / 8 / W, LB = BN / 8 / W;        // 1 KB DMA loads per wave per stage
+  static_assert(LA * 8 * W == BM && LB * 8 * W == BN, "tile/waves mismatch");
 
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[STAGE_A];
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[STAGE_A];
-  __shared__ __attribute__((aligned(1024))) uint16_t sA2[STAGE_A];
-  __shared__ __attribute__((aligned(1024))) uint16_t sA3[STAGE_A];
   __shared__ __attribute__((aligned(1024))) uint16_t sB0[STAGE_B];
   __shared__ __attribute__((aligned(1024))) uint16_t sB1[STAGE_B];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB2[STAGE_B];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB3[STAGE_B];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -100,37 +99,33 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
   const int tile_n = in_group / gsz;
   const int m0 = tile_m * BM, n0 = tile_n * BN;
 
-  // ---- per-lane global sources of the DMA loads (rows clamped in bounds)
+  // ---- per-lane global sources of the DMA loads (rows clamped in bounds):
+  // LDS slot s of a stage holds row s / 8, 16-byte chunk (s % 8) ^ swz(row).
   const uint16_t* ga[LA];
   const uint16_t* gb[LB];
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
-    const int slot = (wave * LA + i) * 64 + lane, row = slot >> 2;
-    const int c = (slot & 3) ^ swz(row);
+    const int slot = (wave * LA + i) * 64 + lane, row = slot >> 3;
+    const int c = (slot & 7) ^ swz(row);
     ga[i] = g.a + static_cast<int64_t>(min(m0 + row, g.M - 1)) * g.lda + c * 8;
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
-    const int slot = (wave * LB + i) * 64 + lane, row = slot >> 2;
-    const int c = (slot & 3) ^ swz(row);
+    const int slot = (wave * LB + i) * 64 + lane, row = slot >> 3;
+    const int c = (slot & 7) ^ swz(row);
     gb[i] = g.w + static_cast<int64_t>(min(n0 + row, g.w_rows - 1)) * g.ldw + c * 8;
   }
   const int nk = g.K / kBK;
 
   auto stageA = [&](auto S) -> uint16_t* {
     if constexpr (decltype(S)::value == 0) return sA0;
-    else if constexpr (decltype(S)::value == 1) return sA1;
-    else if constexpr (decltype(S)::value == 2) return sA2;
-    else return sA3;
+    else return sA1;
   };
   auto stageB = [&](auto S) -> uint16_t* {
     if constexpr (decltype(S)::value == 0) return sB0;
-    else if constexpr (decltype(S)::value == 1) return sB1;
-    else if constexpr (decltype(S)::value == 2) return sB2;
-    else return sB3;
+    else return sB1;
   };
-  // Issue the DMA loads of K step `kstep` (clamped to the last step, so the
-  // count of loads in flight is the same on every step) into stage S.
+  // Issue the DMA loads of K step `kstep` (clamped to the last step) into stage S.
   auto issue = [&](auto S, int kstep) {
     const int koff = min(kstep, nk - 1) * kBK;
     uint16_t* a = stageA(S);
@@ -151,50 +146,69 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
 
-  auto compute = [&](auto S) {
+  // Fragments of one 16-wide k slice of a stage.
+  auto read_frags = [&](auto S, int ks, bf16x8_t (&fa)[TM], bf16x8_t (&fb)[TN]) {
     const uint16_t* a = stageA(S);
     const uint16_t* b = stageB(S);
+    const int c = ks * 2 + (lane >> 5);
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int c = ks * 2 + (lane >> 5);
-      bf16x8_t fa[TM], fb[TN];
+    for (int tm = 0; tm < TM; ++tm) {
+      const int row = wm * WTM + tm * 32 + (lane & 31);
+      fa[tm] = *reinterpret_cast<const bf16x8_t*>(a + row * kBK + ((c ^ swz(row)) << 3));
+    }
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) {
-        const int row = wm * WTM + tm * 32 + (lane & 31);
-        fa[tm] = *reinterpret_cast<const bf16x8_t*>(a + row * kBK + ((c ^ swz(row)) << 3));
-      }
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const int row = wn * WTN + tn * 32 + (lane & 31);
-        fb[tn] = *reinterpret_cast<const bf16x8_t*>(b + row * kBK + ((c ^ swz(row)) << 3));
-      }
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-          acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[tn], fa[tm], acc[tm][tn], 0, 0, 0);
+    for (int tn = 0; tn < TN; ++tn) {
+      const int row = wn * WTN + tn * 32 + (lane & 31);
+      fb[tn] = *reinterpret_cast<const bf16x8_t*>(b + row * kBK + ((c ^ swz(row)) << 3));
     }
   };
-  // One K step on stage S: wait for this wave's loads of the step (two later
-  // steps' loads may stay in flight), barrier (everyone's loads landed, and
-  // everyone finished the previous step, whose stage is reloaded now), then
-  // MFMAs.
+  auto mfmas = [&](const bf16x8_t (&fa)[TM], const bf16x8_t (&fb)[TN]) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[tn], fa[tm], acc[tm][tn], 0, 0, 0);
+  };
+
+  // One K step on stage S: wait for this wave's loads of the step, barrier
+  // (everyone's loads landed; everyone finished the previous step, whose
+  // stage now receives the next step's loads), then four k slices with the
+  // fragment reads of slice j+1 in flight while slice j multiplies.
+  // sched_barrier(0) fences keep the compiler from sinking each read next to
+  // its first use; the explicit lgkmcnt(0) before each batch of reads retires
+  // the previous batch, so no wait lands between reads and the MFMAs they
+  // overlap.
+  bf16x8_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
   auto step = [&](auto S, int kt) {
-    wait_vmcnt<2 * (LA + LB)>();
+    constexpr int s = decltype(S)::value;
+    wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    issue(IC<(decltype(S)::value + 3) % 4>{}, kt + 3);
-    compute(S);
+    issue(IC<s ^ 1>{}, kt + 1);
+    read_frags(S, 0, fa0, fb0);
+    wait_lgkmcnt0();
+    read_frags(S, 1, fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkmcnt0();
+    read_frags(S, 2, fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkmcnt0();
+    read_frags(S, 3, fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkmcnt0();
+    mfmas(fa1, fb1);
   };
 
   issue(IC<0>{}, 0);
-  issue(IC<1>{}, 1);
-  issue(IC<2>{}, 2);
-  // K is a multiple of 4 steps (128), so the ring unrolls without early exits
-  for (int kt = 0; kt < nk; kt += 4) {
+  // K is a multiple of two steps (128), so the ring unrolls without early exits
+  for (int kt = 0; kt < nk; kt += 2) {
     step(IC<0>{}, kt);
     step(IC<1>{}, kt + 1);
-    step(IC<2>{}, kt + 2);
-    step(IC<3>{}, kt + 3);
   }
   wait_vmcnt<0>();  // drain the clamped tail loads before the epilogue
 
