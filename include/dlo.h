@@ -49,8 +49,9 @@
  * LayerNorm has no affine parameters and eps 1e-6; attention is non-causal
  * multi-head softmax(q k^T / sqrt(d / heads)) v.  Between blocks of different
  * width the residual keeps its first min(d_in, d_out) features and zero-fills
- * the rest.  GEMM and attention operands are bf16 with fp32 accumulation; the
- * residual x and the modulation vectors stay fp32.
+ * the rest.  Weights stay the streamed bf16 values (widened exactly to fp16 in
+ * registers); activations between kernels are fp16; matrix-core accumulation,
+ * softmax, the residual x and the modulation vectors are fp32.
  */
 #ifndef DLO_H
 #define DLO_H

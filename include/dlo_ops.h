@@ -4,7 +4,11 @@
  * Each call launches exactly the kernel dlo_forward launches for that step,
  * on the caller's stream, without a context.  They exist so each step can be
  * checked against the oracle and timed on its own.  All pointers are device
- * pointers; bf16 values are their 16-bit patterns.  Calls are asynchronous
+ * pointers; bf16 and fp16 values are their 16-bit patterns.  Weights are
+ * bf16 (as streamed); activations between kernels are fp16 (fp16 has three
+ * more mantissa bits than bf16 and runs the matrix cores at the same rate;
+ * with bf16 activations the rounding error of the widest block reaches the
+ * 2e-2 output tolerance).  Calls are asynchronous
  * with respect to the host.  Shapes are validated on the host before any
  * launch (DLO_E_INVAL / DLO_E_SHAPE, nothing enqueued); a failed launch
  * returns DLO_E_HIP.  Error messages come from dlo_last_error().
@@ -37,7 +41,7 @@ DLO_API dlo_status dlo_op_adaln(const uint16_t* w, const uint16_t* b, const floa
 /* LayerNorm (no affine, eps 1e-6, population variance) + modulation:
  * for each token t, y = adapt(xin[t]) where xin rows have width d_in and
  * adapt keeps the first min(d_in, d) features and zero-fills the rest;
- * h[t][j] = bf16(LN(y)[j] * (1 + scale[j]) + shift[j]).  If xout is not NULL
+ * h[t][j] = fp16(LN(y)[j] * (1 + scale[j]) + shift[j]).  If xout is not NULL
  * the adapted row y (fp32, width d) is written to xout[t] as well (the
  * residual handed to a block of another width).  d must be a multiple of 4
  * and at most 8192; d_in a multiple of 4. */
@@ -45,32 +49,36 @@ DLO_API dlo_status dlo_op_ln_modulate(const float* xin, int32_t d_in, float* xou
                                       const float* shift, const float* scale, uint16_t* h,
                                       int32_t tokens, int32_t d, hipStream_t stream);
 
-/* GEMM on MFMA: acc[i][j] = sum_k a[i][k] * w[j][k] (bf16 operands, fp32
- * accumulation) for i in [0, M), j in [0, N); rows of w at or past w_rows are
- * read as row w_rows - 1 (so padded output columns stay finite).  Epilogues
- * (bf16 results rounded to nearest even):
- *   DLO_EPI_BIAS_BF16      out bf16 [M][ldo]:  out[i][j] = acc + bias[j]
- *   DLO_EPI_BIAS_GELU_BF16 out bf16 [M][ldo]:  out[i][j] = gelu_tanh(acc + bias[j])
+/* GEMM on MFMA: acc[i][j] = sum_k a[i][k] * w[j][k] for i in [0, M), j in
+ * [0, N), fp32 accumulation.  One operand is a weight matrix (bf16, widened to
+ * fp16 in registers), the other fp16 activations: for DLO_EPI_VT_F16 `a` is
+ * the weight and `w` the activation, for every other epilogue `a` is the
+ * activation and `w` the weight.  Rows of w at or past w_rows are read as row
+ * w_rows - 1 (so padded output columns stay finite).  Epilogues (fp16
+ * results rounded to nearest even):
+ *   DLO_EPI_BIAS_F16       out fp16 [M][ldo]:  out[i][j] = acc + bias[j]
+ *   DLO_EPI_BIAS_GELU_F16  out fp16 [M][ldo]:  out[i][j] = gelu_tanh(acc + bias[j])
  *   DLO_EPI_GATED_F32      out fp32 [M][ldo]:  out[i][j] += gate[j] * (acc + bias[j])
- *   DLO_EPI_ROWBIAS_BF16   out bf16 [M][ldo]:  out[i][p(j)] = acc + bias[i]
+ *   DLO_EPI_VT_F16         out fp16 [M][ldo]:  out[i][p(j)] = acc + bias[i]
  * where p(j) swaps bits 2 and 3 of j (the transposed v layout attention
  * reads, see dlo_op_attention).  bias is bf16, gate fp32.  M >= 1; N a
  * multiple of 16; K a multiple of 128; lda, ldw multiples of 8 and >= K;
  * ldo a multiple of 4 and >= N; 1 <= w_rows <= N; a, w 16-byte aligned, out
  * 8-byte (16 for the fp32 epilogue), bias 8-byte (column bias), gate
  * 16-byte. */
-#define DLO_EPI_BIAS_BF16 0
-#define DLO_EPI_BIAS_GELU_BF16 1
+#define DLO_EPI_BIAS_F16 0
+#define DLO_EPI_BIAS_GELU_F16 1
 #define DLO_EPI_GATED_F32 2
-#define DLO_EPI_ROWBIAS_BF16 3
+#define DLO_EPI_VT_F16 3
 DLO_API dlo_status dlo_op_gemm(int32_t epilogue, const uint16_t* a, int32_t lda, const uint16_t* w,
                                int32_t ldw, int32_t w_rows, const uint16_t* bias, const float* gate,
                                void* out, int32_t ldo, int32_t M, int32_t N, int32_t K,
                                hipStream_t stream);
 
 /* Non-causal multi-head attention on MFMA with online softmax:
- * for head h and token t, o[t][h*hd + i] = bf16(sum_s p[t][s] v[s][h*hd + i])
- * with p = softmax_s(q[t] . k[s] / sqrt(hd)), fp32 softmax and accumulation.
+ * for head h and token t, o[t][h*hd + i] = fp16(sum_s p[t][s] v[s][h*hd + i])
+ * with p = softmax_s(q[t] . k[s] / sqrt(hd)), fp32 softmax and accumulation;
+ * q, k, v and the probabilities enter the matrix cores as fp16.
  * q[t][c] = qk[t*ld_qk + c] and k[t][c] = qk[t*ld_qk + heads*hd + c]
  * (the q and k thirds of the QKV projection, row-major); v is given
  * transposed with its keys permuted inside every aligned group of 16:

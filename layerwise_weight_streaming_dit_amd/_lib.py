@@ -25,7 +25,7 @@ FLAG_TRACE, FLAG_SERIALIZE, FLAG_POISON_SLOTS, FLAG_TRACE_KERNELS = 0x1, 0x2, 0x
 IV_H2D, IV_ASM, IV_COMPUTE = 0, 1, 2
 IV_NAMES = {0: "h2d", 1: "asm", 2: "compute", 3: "k_adaln", 4: "k_ln1", 5: "k_qk", 6: "k_v", 7: "k_attn",
             8: "k_out", 9: "k_ln2", 10: "k_fc1", 11: "k_fc2"}
-EPI_BIAS_BF16, EPI_BIAS_GELU_BF16, EPI_GATED_F32, EPI_ROWBIAS_BF16 = 0, 1, 2, 3
+EPI_BIAS_F16, EPI_BIAS_GELU_F16, EPI_GATED_F32, EPI_VT_F16 = 0, 1, 2, 3
 
 
 class DloError(RuntimeError):

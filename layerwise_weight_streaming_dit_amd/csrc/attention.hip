@@ -4,14 +4,17 @@
 // LDS.
 //
 // Orientation.  A wave owns 32 queries of one head and computes the scores
-// transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: K rows are the A
+// transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_f16: K rows are the A
 // operand (8 consecutive head-dim values per lane), the wave's Q rows the B
 // operand (kept in registers for the whole key loop).  In the 32x32 result,
 // lane l holds query (l % 32) and 16 of the 32 keys, so the softmax state of
 // a query lives in one lane pair (l, l ^ 32): row max and row sum need one
 // cross-half exchange and no LDS.
 //
-// The output is accumulated transposed too, O^T += V^T P^T: P (bf16) is the B
+// Operands are fp16 (q, k, v as written by the projections, P converted from
+// the fp32 probabilities), accumulation and softmax fp32.
+//
+// The output is accumulated transposed too, O^T += V^T P^T: P (fp16) is the B
 // operand straight from the S^T registers, and V^T is the A operand.  In the
 // S^T layout, lane group g = l / 32 holds key offsets {8a + 4g + b} (a in
 // {0,1}, b in 0..3) of each 16-key group; the v projection writes V^T with
@@ -19,10 +22,10 @@
 // 8 keys are one aligned 16-byte run and staging is a plain copy.
 //
 // Softmax work per score: one max, one FMA (scale and max folded), one exp2,
-// one add, half a v_cvt_pk_bf16_f32.  The output is rescaled only when a
+// one add, half a v_cvt_pk_f16_f32.  The output is rescaled only when a
 // query's max grows by more than 2^8 over the reference it uses (a
 // wave-uniform branch, usually taken on the first tile only): the
-// probabilities are then at most 256 -- exact in fp32 and in range for bf16 --
+// probabilities are then at most 256 -- exact in fp32 and in range for fp16 --
 // and the final division by the running sum is unchanged, so the result is
 // the same softmax.  Key masking runs only in the last, partial tile.
 //
@@ -67,12 +70,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(
   const int64_t kcol = static_cast<int64_t>(H) * HD + static_cast<int64_t>(h) * HD;
 
   // Q fragments (B operand of S^T = K Q^T).
-  bf16x8_t qf[NKK];
+  f16x8_t qf[NKK];
   {
     const int qrow = min(q0 + kc, T - 1);
     const uint16_t* qp = qk + static_cast<int64_t>(qrow) * ld_qk + static_cast<int64_t>(h) * HD + 8 * g;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qp + kk * 16);
+    for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const f16x8_t*>(qp + kk * 16);
   }
 
   // Staging addresses.
@@ -129,8 +132,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         const int c = kk * 2 + g;
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sK[cur][krow * HD + ((c ^ (krow & KSWZ)) << 3)]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[kb], 0, 0, 0);
+        const f16x8_t a = *reinterpret_cast<const f16x8_t*>(&sK[cur][krow * HD + ((c ^ (krow & KSWZ)) << 3)]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[kk], s[kb], 0, 0, 0);
       }
     }
     // ---- max over raw scores (the scale is positive)
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(
       m_use = m_new;
     }
     const float nm = -m_use;
-    bf16x8_t pb[2][2];
+    f16x8_t pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -169,9 +172,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(
           const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * ks + 2 * e], scale_log2, nm));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * ks + 2 * e + 1], scale_log2, nm));
           l_run += p0 + p1;
-          w[e] = pack_bf16x2(p0, p1);
+          w[e] = pack_f16x2(p0, p1);
         }
-        pb[kb][ks] = __builtin_bit_cast(bf16x8_t, w);
+        pb[kb][ks] = __builtin_bit_cast(f16x8_t, w);
       }
     // ---- O^T += V^T P^T
 #pragma unroll
@@ -182,8 +185,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int c = kb * 4 + ks * 2 + g;
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sV[cur][vrow * kBKV + ((c ^ (vrow & 7)) << 3)]);
-          oacc[ib] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kb][ks], oacc[ib], 0, 0, 0);
+          const f16x8_t a = *reinterpret_cast<const f16x8_t*>(&sV[cur][vrow * kBKV + ((c ^ (vrow & 7)) << 3)]);
+          oacc[ib] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[kb][ks], oacc[ib], 0, 0, 0);
         }
     }
   };
@@ -219,8 +222,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         u32x2_t w;
-        w.x = pack_bf16x2(oacc[ib][4 * rg] * inv, oacc[ib][4 * rg + 1] * inv);
-        w.y = pack_bf16x2(oacc[ib][4 * rg + 2] * inv, oacc[ib][4 * rg + 3] * inv);
+        w.x = pack_f16x2(oacc[ib][4 * rg] * inv, oacc[ib][4 * rg + 1] * inv);
+        w.y = pack_f16x2(oacc[ib][4 * rg + 2] * inv, oacc[ib][4 * rg + 3] * inv);
         *reinterpret_cast<u32x2_t*>(op + ib * 32 + 8 * rg) = w;
       }
   }

@@ -7,29 +7,37 @@
 namespace dlo {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // bf16 bit pattern -> fp32 (exact: bf16 is the upper half of an fp32).
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16 bit pattern, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+// Two fp32 -> packed pair of fp16 (lo in bits 0..15), round to nearest even
+// (v_cvt_pk_f16_f32).  Activations between kernels are fp16.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2_t v = __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// Two fp32 -> packed pair of bf16 (lo in bits 0..15), round to nearest even,
-// with gfx950's v_cvt_pk_bf16_f32 (one instruction per pair).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const bf16x2_t v = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
-  return __builtin_bit_cast(uint32_t, v);
+// Eight bf16 weights -> eight fp16 operands for the fp16 matrix cores.  A bf16
+// value has 8 significant bits and fp16 has 11, so the widening is exact for
+// every weight of magnitude >= 2^-14; smaller ones become fp16 subnormals
+// (absolute error <= 2^-25).
+__device__ __forceinline__ f16x8_t bf16x8_to_f16x8(bf16x8_t v) {
+  const u32x4_t w = __builtin_bit_cast(u32x4_t, v);
+  u32x4_t o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = pack_f16x2(__uint_as_float(w[i] << 16), __uint_as_float(w[i] & 0xffff0000u));
+  return __builtin_bit_cast(f16x8_t, o);
 }
 
 // Column position of token j in the transposed v buffer: inside every aligned

@@ -18,7 +18,7 @@ hipError_t launch_adaln(const uint16_t* w, const uint16_t* b, const float* cond,
 hipError_t launch_ln_modulate(const float* xin, int d_in, float* xout, const float* shift,
                               const float* scale, uint16_t* h, int tokens, int d, hipStream_t s);
 
-enum Epilogue { EPI_BIAS_BF16 = 0, EPI_BIAS_GELU_BF16 = 1, EPI_GATED_F32 = 2, EPI_ROWBIAS_BF16 = 3 };
+enum Epilogue { EPI_BIAS_F16 = 0, EPI_BIAS_GELU_F16 = 1, EPI_GATED_F32 = 2, EPI_VT_F16 = 3 };
 
 struct GemmArgs {
   const uint16_t* a;

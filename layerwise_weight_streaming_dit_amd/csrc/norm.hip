@@ -93,8 +93,8 @@ __global__ __launch_bounds__(THREADS) void ln_modulate_kernel(
       const f32x4_t sc = *reinterpret_cast<const f32x4_t*>(scale + q * 4);
       const f32x4_t y = (v[i] - mean) * rstd * (1.0f + sc) + sh;
       u32x2_t o;
-      o.x = pack_bf16x2(y.x, y.y);
-      o.y = pack_bf16x2(y.z, y.w);
+      o.x = pack_f16x2(y.x, y.y);
+      o.y = pack_f16x2(y.z, y.w);
       *reinterpret_cast<u32x2_t*>(h + t * d + q * 4) = o;
       if (xout != nullptr) *reinterpret_cast<f32x4_t*>(xout + t * d + q * 4) = v[i];
     }

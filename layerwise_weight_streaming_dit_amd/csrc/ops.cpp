@@ -59,7 +59,7 @@ extern "C" DLO_API dlo_status dlo_op_gemm(int32_t epilogue, const uint16_t* a, i
                                           void* out, int32_t ldo, int32_t M, int32_t N, int32_t K,
                                           hipStream_t s) {
   clear_error();
-  if (epilogue < DLO_EPI_BIAS_BF16 || epilogue > DLO_EPI_ROWBIAS_BF16)
+  if (epilogue < DLO_EPI_BIAS_F16 || epilogue > DLO_EPI_VT_F16)
     return fail(DLO_E_INVAL, "unknown epilogue %d", epilogue);
   if (!a || !w || !bias || !out) return fail(DLO_E_INVAL, "NULL pointer");
   if (epilogue == DLO_EPI_GATED_F32 && !gate) return fail(DLO_E_INVAL, "gate is NULL");
@@ -70,7 +70,7 @@ extern "C" DLO_API dlo_status dlo_op_gemm(int32_t epilogue, const uint16_t* a, i
   if (ldo < N || ldo % 4) return fail(DLO_E_SHAPE, "ldo %d must be >= N %d and a multiple of 4", ldo, N);
   if (!aligned(a, 16) || !aligned(w, 16)) return fail(DLO_E_INVAL, "operands must be 16-byte aligned");
   const size_t oal = epilogue == DLO_EPI_GATED_F32 ? 16 : 8;
-  if (!aligned(out, oal) || !aligned(bias, epilogue == DLO_EPI_ROWBIAS_BF16 ? 2 : 8) ||
+  if (!aligned(out, oal) || !aligned(bias, epilogue == DLO_EPI_VT_F16 ? 2 : 8) ||
       (gate && !aligned(gate, 16)))
     return fail(DLO_E_INVAL, "out, bias or gate misaligned for vector access");
   GemmArgs g{a, w, bias, gate, out, lda, ldw, ldo, M, N, K, w_rows};

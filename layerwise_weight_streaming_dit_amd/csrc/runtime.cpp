@@ -334,10 +334,10 @@ dlo_status enqueue_block_compute(dlo_ctx* ctx, int b, float*& x_cur, int& d_cur,
   }
   // q, k projection: qk[T][2d] = h Wqk^T + bqk
   const GemmArgs gqk{w.h, Wqkv, bqkv, nullptr, w.qk, d, d, 2 * d, T, 2 * d, d, 2 * d};
-  DLO_STEP(DLO_IV_K_QK, launch_gemm(EPI_BIAS_BF16, gqk, s));
+  DLO_STEP(DLO_IV_K_QK, launch_gemm(EPI_BIAS_F16, gqk, s));
   // v projection, transposed: vt[d][Tp] = Wv h^T + bv (columns >= T finite)
   const GemmArgs gv{Wqkv + int64_t(2) * d * d, w.h, bqkv + 2 * d, nullptr, w.vt, d, d, Tp, d, Tp, d, T};
-  DLO_STEP(DLO_IV_K_V, launch_gemm(EPI_ROWBIAS_BF16, gv, s));
+  DLO_STEP(DLO_IV_K_V, launch_gemm(EPI_VT_F16, gv, s));
   DLO_STEP(DLO_IV_K_ATTN, launch_attention(w.qk, 2 * d, w.vt, Tp, w.o, d, T, H, hd, s));
   // x += gate1 * (o Wo^T + bo)
   const GemmArgs go{w.o, Wo, bo, mod + 2 * d, x_cur, d, d, d, T, d, d, d};
@@ -345,7 +345,7 @@ dlo_status enqueue_block_compute(dlo_ctx* ctx, int b, float*& x_cur, int& d_cur,
   DLO_STEP(DLO_IV_K_LN2, launch_ln_modulate(x_cur, d, nullptr, mod + 3 * d, mod + 4 * d, w.h, T, d, s));
   // u = gelu(h2 W1^T + b1)
   const GemmArgs g1{w.h, W1, b1, nullptr, w.u, d, d, m, T, m, d, m};
-  DLO_STEP(DLO_IV_K_FC1, launch_gemm(EPI_BIAS_GELU_BF16, g1, s));
+  DLO_STEP(DLO_IV_K_FC1, launch_gemm(EPI_BIAS_GELU_F16, g1, s));
   // x += gate2 * (u W2^T + b2)
   const GemmArgs g2{w.u, W2, b2, mod + 5 * d, x_cur, m, m, d, T, d, m, d};
   DLO_STEP(DLO_IV_K_FC2, launch_gemm(EPI_GATED_F32, g2, s));

@@ -38,3 +38,20 @@ def within(got, want, rtol=RTOL, atol=ATOL):
     ok = bool(np.all(err <= atol + rtol * np.abs(want))) and bool(np.all(np.isfinite(got)))
     rel = err / np.maximum(np.abs(want), 1e-30)
     return ok, float(err.max(initial=0.0)), float(rel.max(initial=0.0))
+
+
+def run_forward(ctx, x, cond):
+    """One streamed forward of x [T, d_first] (numpy fp32) through a context;
+    returns the [T, d_last] result as numpy."""
+    t = torch()
+    T, d0 = x.shape
+    xbuf = t.zeros(T * ctx.max_d, dtype=t.float32, device="cuda")
+    xbuf[: T * d0] = dev(np.ascontiguousarray(x, np.float32).reshape(-1))
+    out = ctx.forward(xbuf, dev(np.asarray(cond, np.float32)), T)
+    t.cuda.synchronize()
+    return host(out).copy()
+
+
+def sample_rows(T, n, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, T - 1], rng.integers(0, T, size=n)]))
