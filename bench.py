@@ -28,7 +28,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 and fp16 MFMA (same rate)
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 PCIE5_X16_GBPS = 64.0       # nominal host link per direction
 
@@ -81,18 +81,18 @@ def source_hash(path):
 
 
 def traffic_from_profiles(kernel_src, kind):
-    """HBM bytes per launch of the dominant kernel from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel source."""
-    p = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    summary (profiles/hbm_traffic_image_dit.txt: lines "kind source-sha16
+    fetch-bytes write-bytes", copy-calibrated), used only if the summary was
+    taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "hbm_traffic_image_dit.txt")
     if not os.path.exists(p):
         return None
-    try:
-        t = json.load(open(p))
-        e = t.get(kind)
-        if e and e.get("source_sha256_16") == source_hash(kernel_src):
-            return e.get("bytes_per_launch")
-    except Exception:
-        return None
+    want = source_hash(kernel_src)
+    for line in open(p):
+        f = line.split()
+        if len(f) == 4 and f[0] == kind and f[1] == want:
+            return float(f[2]) + float(f[3])
     return None
 
 
@@ -140,6 +140,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-serial", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 256 MiB device copy (the reconstruction kernel) so "
+                         "a counter pass can scale HBM byte counters by a copy of known size")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -155,6 +158,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = 1 << 27  # elements: 256 MiB read + 256 MiB written
+        src = torch.empty(n, dtype=torch.int16, device="cuda").fill_(1)
+        dst = torch.empty(n, dtype=torch.int16, device="cuda")
+        torch.cuda.synchronize()
+        dlo.op_assemble(dst, src, n)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy: {2 * n} bytes read, {2 * n} bytes written", file=sys.stderr, flush=True)
+        del src, dst
     wl = synth.workload(args.workload)
     shapes = list(wl.blocks)
     dp = args.dp or wl.dp_sizes[0]
@@ -325,7 +337,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp16",
+        "precision": "weights bf16 (streamed, reconstructed bit-exact, widened to fp16 in registers); "
+                     "fp16 matrix-core operands; fp32 accumulation, softmax, residual and modulation",
         "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) activations)",
         "config": {"workload": wl.description, "blocks": L, "d_model": shp.d_model, "heads": shp.n_heads,
                    "d_mlp": shp.d_mlp, "d_cond": shp.d_cond, "tokens": T, "batch": 1, "dp_size": dp,
