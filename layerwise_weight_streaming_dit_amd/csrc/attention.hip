@@ -65,8 +65,22 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5;
   const int kc = lane & 31;
-  const int h = blockIdx.y;
-  const int q0 = blockIdx.x * kBQ + wave * 32;
+  // Workgroups are dispatched round-robin over the 8 XCDs (workgroup i to XCD
+  // i % 8).  When the head count is a multiple of 8, head h runs entirely on
+  // XCD h % 8, one head at a time per XCD, so its K and V are fetched from
+  // HBM into that XCD's L2 once instead of once per XCD.
+  const int nq = (T + kBQ - 1) / kBQ;
+  const int bid = blockIdx.x;
+  int h, qt;
+  if ((H & 7) == 0) {
+    const int xcd = bid & 7, local = bid >> 3;
+    h = (local / nq) * 8 + xcd;
+    qt = local % nq;
+  } else {
+    h = bid / nq;
+    qt = bid % nq;
+  }
+  const int q0 = qt * kBQ + wave * 32;
   const int64_t kcol = static_cast<int64_t>(H) * HD + static_cast<int64_t>(h) * HD;
 
   // Q fragments (B operand of S^T = K Q^T).
@@ -234,7 +248,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(
 hipError_t launch_attention(const uint16_t* qk, int ld_qk, const uint16_t* vt, int ld_vt, uint16_t* o,
                             int ld_o, int tokens, int heads, int head_dim, hipStream_t s) {
   if (tokens <= 0) return hipSuccess;
-  const dim3 grid((tokens + kBQ - 1) / kBQ, heads), block(kAttnThreads);
+  const dim3 grid(((tokens + kBQ - 1) / kBQ) * heads), block(kAttnThreads);
   const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(head_dim)));
   if (head_dim == 128)
     hipLaunchKernelGGL(attention_kernel<128>, grid, block, 0, s, qk, ld_qk, vt, ld_vt, o, ld_o, tokens,
