@@ -112,7 +112,8 @@ typedef struct dlo_config {
   int32_t num_blocks;          /* >= 1 */
   const dlo_block_desc* blocks;/* num_blocks entries, copied by dlo_create */
   int32_t dp_size;             /* number of shards per block, >= 1 */
-  int32_t max_tokens;          /* largest token count dlo_forward accepts, >= 1 */
+  int32_t max_tokens;          /* largest token count dlo_forward accepts, in [1, 2^20], and
+                                  max_tokens * max(d_model, d_mlp) * 2 bytes below 4 GiB */
   int64_t landing_chunk_elems; /* H2D chunk size in elements; 0 = default
                                   min(max shard size, 2^24); else >= 4096 */
   int32_t device;              /* HIP device ordinal the context runs on */

@@ -69,6 +69,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // s_waitcnt lgkmcnt(0) leaving vmcnt / expcnt unconstrained.
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
+// base + 32-bit byte offset (lets the loads use an SGPR base with a VGPR offset)
+__device__ __forceinline__ const uint16_t* at(const uint16_t* base, uint32_t byte_off) {
+  return reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+
 template <int V>
 using IC = std::integral_constant<int, V>;
 
@@ -110,19 +115,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
 
   // ---- per-lane global sources of the DMA loads (rows clamped in bounds):
   // LDS slot s of a stage holds row s / 8, 16-byte chunk (s % 8) ^ swz(row).
-  const uint16_t* ga[LA];
-  const uint16_t* gb[LB];
+  uint32_t ga[LA], gb[LB];  // byte offsets from g.a / g.w (host checks they fit 32 bits)
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
     const int slot = (wave * LA + i) * 64 + lane, row = slot >> 3;
     const int c = (slot & 7) ^ swz(row);
-    ga[i] = g.a + static_cast<int64_t>(min(m0 + row, g.M - 1)) * g.lda + c * 8;
+    ga[i] = (static_cast<uint32_t>(min(m0 + row, g.M - 1)) * g.lda + c * 8) * 2u;
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
     const int slot = (wave * LB + i) * 64 + lane, row = slot >> 3;
     const int c = (slot & 7) ^ swz(row);
-    gb[i] = g.w + static_cast<int64_t>(min(n0 + row, g.w_rows - 1)) * g.ldw + c * 8;
+    gb[i] = (static_cast<uint32_t>(min(n0 + row, g.w_rows - 1)) * g.ldw + c * 8) * 2u;
   }
   const int nk = g.K / kBK;
 
@@ -134,17 +138,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
     if constexpr (decltype(S)::value == 0) return sB0;
     else return sB1;
   };
-  // Issue the DMA loads of K step `kstep` (clamped to the last step) into stage S.
+  // DMA load d of K step `kstep` (clamped to the last step) into stage S:
+  // d < LA are this wave's A loads, the rest its W loads.
+  auto issue_one = [&](auto S, int kstep, int d) {
+    const uint32_t koff = static_cast<uint32_t>(min(kstep, nk - 1)) * (kBK * 2);
+    if (d < LA)
+      dma16(at(g.a, ga[d] + koff), stageA(S) + (wave * LA + d) * 512);
+    else
+      dma16(at(g.w, gb[d - LA] + koff), stageB(S) + (wave * LB + d - LA) * 512);
+  };
   auto issue = [&](auto S, int kstep) {
-    const int koff = min(kstep, nk - 1) * kBK;
-    uint16_t* a = stageA(S);
-    uint16_t* b = stageB(S);
 #pragma unroll
-    for (int i = 0; i < LA; ++i)
-      dma16(ga[i] + koff, a + (wave * LA + i) * 512);
-#pragma unroll
-    for (int i = 0; i < LB; ++i)
-      dma16(gb[i] + koff, b + (wave * LB + i) * 512);
+    for (int d = 0; d < LA + LB; ++d) issue_one(S, kstep, d);
   };
 
   f32x16_t acc[TM][TN];
@@ -173,7 +178,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
   };
   // The weight operand (bf16) is widened to fp16 in registers, once per
   // fragment; the activation operand is already fp16.
-  auto mfmas = [&](const bf16x8_t (&fa)[TM], const bf16x8_t (&fb)[TN]) {
+  // `after_row(tm)` runs after the MFMAs of tile row tm (used to interleave
+  // the next step's DMA loads with the matrix work).
+  auto mfmas = [&](const bf16x8_t (&fa)[TM], const bf16x8_t (&fb)[TN], auto&& after_row) {
     f16x8_t a16[TM], b16[TN];
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
@@ -182,11 +189,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
     for (int tn = 0; tn < TN; ++tn)
       b16[tn] = A_IS_WEIGHT ? __builtin_bit_cast(f16x8_t, fb[tn]) : bf16x8_to_f16x8(fb[tn]);
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
+    for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
         acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b16[tn], a16[tm], acc[tm][tn], 0, 0, 0);
+      after_row(tm);
+    }
   };
+  auto nothing = [](int) {};
 
   // One K step on stage S: wait for this wave's loads of the step, barrier
   // (everyone's loads landed; everyone finished the previous step, whose
@@ -197,29 +207,42 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
   // the previous batch, so no wait lands between reads and the MFMAs they
   // overlap.
   bf16x8_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+  // The next step's LA + LB DMA loads are spread over the tile rows of the
+  // first two k slices (kPer after each row), so no wave stalls on a full
+  // address queue while it has MFMAs to issue.
+  constexpr int kSlots = 2 * TM, kPer = (LA + LB + kSlots - 1) / kSlots;
   auto step = [&](auto S, int kt) {
     constexpr int s = decltype(S)::value;
+    auto dma_after = [&](int slot) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int d = slot * kPer + j;
+        if (d < LA + LB) {
+          issue_one(IC<s ^ 1>{}, kt + 1, d);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    issue(IC<s ^ 1>{}, kt + 1);
     read_frags(S, 0, fa0, fb0);
     wait_lgkmcnt0();
     read_frags(S, 1, fa1, fb1);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(fa0, fb0);
+    mfmas(fa0, fb0, [&](int tm) { dma_after(tm); });
     __builtin_amdgcn_sched_barrier(0);
     wait_lgkmcnt0();
     read_frags(S, 2, fa0, fb0);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(fa1, fb1);
+    mfmas(fa1, fb1, [&](int tm) { dma_after(TM + tm); });
     __builtin_amdgcn_sched_barrier(0);
     wait_lgkmcnt0();
     read_frags(S, 3, fa1, fb1);
     __builtin_amdgcn_sched_barrier(0);
-    mfmas(fa0, fb0);
+    mfmas(fa0, fb0, nothing);
     __builtin_amdgcn_sched_barrier(0);
     wait_lgkmcnt0();
-    mfmas(fa1, fb1);
+    mfmas(fa1, fb1, nothing);
   };
 
   issue(IC<0>{}, 0);

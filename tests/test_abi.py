@@ -107,6 +107,13 @@ def test_invalid_block_shapes_rejected(bad):
         dlo.block_layout(bad, 4)
 
 
+def test_activations_beyond_4gib_rejected():
+    # 2^20 tokens x d_mlp 8192 x 2 bytes = 16 GiB: GEMM offsets are 32-bit
+    cfg, keep = _cfg([synth.BlockShape(256, 4, 8192)], max_tokens=1 << 20, arena=256, arena_bytes=1 << 40)
+    assert _create_status(cfg)[0] == L.E_INVAL
+    assert "4 GiB" in L.lib().dlo_last_error().decode()
+
+
 def test_abi_version_and_mixed_cond_rejected():
     cfg, keep = _cfg(TINY, arena=256, arena_bytes=1 << 40)
     cfg.abi_version = 99
@@ -131,6 +138,10 @@ def test_op_validation_without_launch():
     assert lib.dlo_op_gemm(0, fake, 128, fake, 128, 24, fake, None, fake, 24, 64, 24, 128, None) == L.E_SHAPE
     assert lib.dlo_op_gemm(9, fake, 128, fake, 128, 64, fake, None, fake, 64, 64, 64, 128, None) == L.E_INVAL
     assert lib.dlo_op_gemm(2, fake, 128, fake, 128, 64, fake, None, fake, 64, 64, 64, 128, None) == L.E_INVAL
+    # operands are addressed with 32-bit byte offsets: more than 2^17 rows x 2^14 elements is beyond 4 GiB
+    assert lib.dlo_op_gemm(0, fake, 1 << 14, fake, 128, 64, fake, None, fake, 64, (1 << 17) + 1, 64, 128, None) == L.E_SHAPE
+    assert lib.dlo_op_gemm(0, fake, 128, fake, 1 << 14, (1 << 17) + 16, fake, None, fake, (1 << 17) + 16, 64, (1 << 17) + 16, 128,
+                           None) == L.E_SHAPE
     assert lib.dlo_op_attention(fake, 256, fake, 64, fake, 128, 10, 1, 96, None) == L.E_SHAPE
     assert lib.dlo_op_attention(fake, 256, fake, 32, fake, 128, 40, 1, 128, None) == L.E_SHAPE
     assert lib.dlo_op_adaln(fake, fake, fake, fake, 10, 100, None) == L.E_SHAPE
