@@ -49,9 +49,12 @@
  * LayerNorm has no affine parameters and eps 1e-6; attention is non-causal
  * multi-head softmax(q k^T / sqrt(d / heads)) v.  Between blocks of different
  * width the residual keeps its first min(d_in, d_out) features and zero-fills
- * the rest.  Weights stay the streamed bf16 values (widened exactly to fp16 in
- * registers); activations between kernels are fp16; matrix-core accumulation,
- * softmax, the residual x and the modulation vectors are fp32.
+ * the rest.  Weights stay the streamed bf16 values, widened to fp16 in
+ * registers for the matrix cores (exact for |w| >= 2^-17; smaller magnitudes
+ * round to fp16's subnormal grid, error <= 2^-25; |w| > 65504 overflows);
+ * biases and the adaLN weights are read as bf16 in fp32 arithmetic;
+ * activations between kernels are fp16; matrix-core accumulation, softmax,
+ * the residual x and the modulation vectors are fp32.
  */
 #ifndef DLO_H
 #define DLO_H

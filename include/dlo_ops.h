@@ -51,7 +51,8 @@ DLO_API dlo_status dlo_op_ln_modulate(const float* xin, int32_t d_in, float* xou
 
 /* GEMM on MFMA: acc[i][j] = sum_k a[i][k] * w[j][k] for i in [0, M), j in
  * [0, N), fp32 accumulation.  One operand is a weight matrix (bf16, widened to
- * fp16 in registers), the other fp16 activations: for DLO_EPI_VT_F16 `a` is
+ * fp16 in registers: exact for |w| >= 2^-17, rounded to fp16's subnormal grid
+ * below, overflowing above 65504), the other fp16 activations: for DLO_EPI_VT_F16 `a` is
  * the weight and `w` the activation, for every other epilogue `a` is the
  * activation and `w` the weight.  Rows of w at or past w_rows are read as row
  * w_rows - 1 (so padded output columns stay finite).  Epilogues (fp16

@@ -21,11 +21,12 @@
 // each XCD a contiguous range of tiles, walked in groups of kGroupM tile rows,
 // so tiles that share A rows or W rows share an L2.
 //
-// Precision: weights are the streamed bf16 values, widened exactly to fp16 in
-// registers; activations are fp16; accumulation is fp32.  (fp16 operands have
-// 3 more mantissa bits than bf16 at the same matrix-core rate; with bf16
-// activations the rounding error of a d = 8192 block reaches the 2e-2 output
-// tolerance.)
+// Precision: weights are the streamed bf16 values, widened to fp16 in
+// registers (exact for |w| >= 2^-17; smaller magnitudes round to fp16's
+// subnormal grid, |w| > 65504 would overflow); activations are fp16;
+// accumulation is fp32.  (fp16 operands have 3 more mantissa bits than bf16
+// at the same matrix-core rate; with bf16 activations the rounding error of a
+// d = 8192 block reaches the 2e-2 output tolerance.)
 //
 // Epilogues fuse the DiT block's elementwise work into the GEMM:
 //   bias -> fp16 (q/k projection), bias + GELU(tanh) -> fp16 (MLP up),
