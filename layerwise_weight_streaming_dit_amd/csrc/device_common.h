@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace dlo {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -65,5 +67,32 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+
+// 16 bytes per lane from global memory straight into LDS: lane i's data lands
+// at lds + 16 * i (global_load_lds_dwordx4).  The LDS address-space cast only
+// exists in the device pass; the host pass sees an empty body.
+__device__ __forceinline__ void dma16(const uint16_t* gsrc, uint16_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+#endif
+}
+
+// s_waitcnt vmcnt(n) leaving lgkmcnt / expcnt unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt lgkmcnt(0) leaving vmcnt / expcnt unconstrained.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+// base + 32-bit byte offset (lets the loads use an SGPR base with a VGPR offset)
+__device__ __forceinline__ const uint16_t* at(const uint16_t* base, uint32_t byte_off) {
+  return reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(base) + byte_off);
+}
+
+template <int V>
+using IC = std::integral_constant<int, V>;
 
 }  // namespace dlo

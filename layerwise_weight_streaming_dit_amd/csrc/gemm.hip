@@ -44,39 +44,12 @@ namespace dlo {
 
 namespace {
 
-// 16 bytes per lane from global memory straight into LDS: lane i's data lands
-// at lds + 16 * i (global_load_lds_dwordx4).  The LDS address-space cast only
-// exists in the device pass; the host pass sees an empty body.
-__device__ __forceinline__ void dma16(const uint16_t* gsrc, uint16_t* lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-#endif
-}
-
 constexpr int kBK = 64;      // K per stage: one full 128-byte line per row
 constexpr int kGroupM = 4;
 
 // 16-byte chunk swizzle of a 128-byte LDS row: keeps the fragment reads of 8
 // (32 banks) or 16 (64 banks) consecutive rows on distinct banks.
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
-
-// s_waitcnt vmcnt(n) leaving lgkmcnt / expcnt unconstrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// s_waitcnt lgkmcnt(0) leaving vmcnt / expcnt unconstrained.
-__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
-
-// base + 32-bit byte offset (lets the loads use an SGPR base with a VGPR offset)
-__device__ __forceinline__ const uint16_t* at(const uint16_t* base, uint32_t byte_off) {
-  return reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(base) + byte_off);
-}
-
-template <int V>
-using IC = std::integral_constant<int, V>;
 
 template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
