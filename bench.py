@@ -307,17 +307,21 @@ def main():
                 "work_per_launch": work, "work_unit": unit}
 
     # synchronous schedule (H2D -> wait -> reconstruct -> wait -> compute), same kernels
-    serial = None
+    serial = enqueue_untraced_us = None
     if not args.no_serial:
         sctx = make(dlo.FLAG_SERIALIZE)
         sctx.forward(xbuf, cond, T)
         torch.cuda.synchronize()
         n_s = max(2, args.steps // 4)
         ts = time.perf_counter()
+        enq_s = 0.0
         for _ in range(n_s):
+            te = time.perf_counter()
             sctx.forward(xbuf, cond, T)
+            enq_s += time.perf_counter() - te
         torch.cuda.synchronize()
         serial = 1e3 * (time.perf_counter() - ts) / n_s
+        enqueue_untraced_us = 1e6 * enq_s / n_s
         sctx.close()
 
     # pinned H2D ceiling with a plain copy of the same size as one block's shards
@@ -372,7 +376,9 @@ def main():
         "gemm_mfma_util": gemm_util,
         "step_boundary": {"isolated_forward_ms": iso_ms, "back_to_back_ms_per_step": ms_per_step,
                           "host_enqueue_us_per_forward": 1e6 * enqueue_s / args.steps,
-                          "host_enqueue_us_per_block": 1e6 * enqueue_s / args.steps / L},
+                          "host_enqueue_us_per_block": 1e6 * enqueue_s / args.steps / L,
+                          "host_enqueue_note": "timed context records HIP events around every kernel",
+                          "host_enqueue_us_per_forward_untraced": enqueue_untraced_us},
         "overlap": {"E": overlap_E, "hidden_frac": hidden, "t_forward_ms": t_fwd, "sum_h2d_ms": h2d_ms,
                     "sum_asm_ms": asm_ms, "sum_compute_ms": comp_ms, "serialized_ms": serial},
         "residency": {"high_water_blocks": st["residency_high_water"], "slot_bytes": st["slot_bytes"],
