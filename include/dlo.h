@@ -221,6 +221,10 @@ DLO_API dlo_status dlo_load_shards(dlo_ctx* ctx, int32_t block, const uint16_t* 
  * its buffer must hold tokens * max_d floats.  cond: device fp32 [d_cond].
  * Enqueues on stream (the compute stream) and the context's side streams and
  * returns without waiting; the result is ready when stream reaches it.
+ * Consecutive blocks alternate slots, and the alternation continues across
+ * calls (block 0 of a call takes the slot the previous call's last block
+ * does not use), so back-to-back calls -- one per denoising step -- stream
+ * the next call's first block while the previous call's last block computes.
  * Errors before any enqueue: DLO_E_STATE if a block has no shards,
  * DLO_E_INVAL if tokens is outside [1, max_tokens] or a pointer is NULL. */
 DLO_API dlo_status dlo_forward(dlo_ctx* ctx, float* x, const float* cond, int32_t tokens,

@@ -20,7 +20,8 @@
 // DMA engines), one per landing buffer: while one engine sets up its next
 // transfer the other keeps the host link busy.
 //
-// Per block b (slot k = b % 2) the host enqueues, without ever blocking:
+// Per block b (slot k = (b + parity) % 2) the host enqueues, without ever
+// blocking:
 //   copy stream j%2: per chunk j: wait land_free[j%2]; H2D -> landing[j%2];
 //                   record h2d_done[j%2]
 //   gather stream : wait comp_done[k] (compute of block b-2 released slot k);
@@ -30,6 +31,10 @@
 //                   record comp_done[k]
 // Events are re-recorded every block; each wait binds to the latest record
 // enqueued before it, which is the intended predecessor in this enqueue order.
+// Consecutive forwards continue the alternation: `parity` flips after a
+// forward with an odd block count, so block 0 of the next forward always goes
+// into the slot the previous forward's last block is not computing from and
+// streams while that block computes.
 #include <string.h>
 
 #include <algorithm>
@@ -99,6 +104,7 @@ struct dlo_ctx {
   size_t slot_bytes = 0, landing_bytes = 0, workspace_bytes = 0;
   std::vector<dlo::Block> blocks;
   uint16_t* slot[2] = {nullptr, nullptr};
+  int parity = 0;  // slot of block 0 in the next forward
   uint16_t* landing[2] = {nullptr, nullptr};
   dlo::Workspace ws;
   hipStream_t copy_s = nullptr, copy_s2 = nullptr, gather_s = nullptr;
@@ -232,12 +238,11 @@ hipEvent_t next_ev(dlo_ctx* ctx) {
   return ctx->ev_pool[ctx->ev_next++];
 }
 
-// Enqueue the H2D + reconstruction of block b into slot b % 2 on the copy and
+// Enqueue the H2D + reconstruction of block b into slot k on the copy and
 // gather streams.  `trace` adds timed intervals; `in_forward` is false for
 // the stand-alone debug path (no compute of block b-1 to wait for).
-dlo_status enqueue_staging(dlo_ctx* ctx, int b, bool trace, bool in_forward) {
+dlo_status enqueue_staging(dlo_ctx* ctx, int b, int k, bool trace, bool in_forward) {
   Block& blk = ctx->blocks[b];
-  const int k = b & 1;
   for (size_t ci = 0; ci < blk.chunks.size(); ++ci) {
     const Chunk& c = blk.chunks[ci];
     const int lb = static_cast<int>(ctx->land_counter & 1);
@@ -286,12 +291,12 @@ dlo_status enqueue_staging(dlo_ctx* ctx, int b, bool trace, bool in_forward) {
   return DLO_OK;
 }
 
-// The DiT block of `b` from slot b % 2 on the compute stream.
-dlo_status enqueue_block_compute(dlo_ctx* ctx, int b, float*& x_cur, int& d_cur, float* x_user,
+// The DiT block of `b` from slot k on the compute stream.
+dlo_status enqueue_block_compute(dlo_ctx* ctx, int b, int k, float*& x_cur, int& d_cur, float* x_user,
                                  const float* cond, int T, hipStream_t s, bool trace) {
   const Block& blk = ctx->blocks[b];
   const BlockLayout& L = blk.layout;
-  const uint16_t* base = ctx->slot[b & 1];
+  const uint16_t* base = ctx->slot[k];
   // parameter re-pointing from the cached offsets
   const uint16_t* Wqkv = base + L.off_wqkv;
   const uint16_t* bqkv = base + L.off_bqkv;
@@ -308,7 +313,6 @@ dlo_status enqueue_block_compute(dlo_ctx* ctx, int b, float*& x_cur, int& d_cur,
   const int Tp = static_cast<int>(align_up(size_t(T), 64));
   const Workspace& w = ctx->ws;
   float* mod = w.mod;
-  const int k = b & 1;
   // Record a timed interval around one kernel when tracing.
   auto timed = [&](int kind, auto&& launch) -> dlo_status {
     TraceEv tv{};
@@ -581,17 +585,18 @@ extern "C" DLO_API dlo_status dlo_forward(dlo_ctx* ctx, float* x, const float* c
   float* x_cur = x;
   int d_cur = ctx->blocks[0].desc.d_model;
   const int L = static_cast<int>(ctx->blocks.size());
+  const int parity = ctx->parity;
   for (int b = 0; b < L; ++b) {
-    st = enqueue_staging(ctx, b, trace_all, true);
+    const int k = (b + parity) & 1;
+    st = enqueue_staging(ctx, b, k, trace_all, true);
     if (st != DLO_OK) return st;
-    const int k = b & 1;
     DLO_HIP(ctx, hipStreamWaitEvent(stream, ctx->asm_done[k], 0));
     TraceEv tc{};
     if (trace) {
       tc = TraceEv{DLO_IV_COMPUTE, b, -1, k, -1, 0, next_ev(ctx), next_ev(ctx)};
       if (tc.start) DLO_HIP(ctx, hipEventRecord(tc.start, stream));
     }
-    st = enqueue_block_compute(ctx, b, x_cur, d_cur, x, cond, tokens, stream, trace);
+    st = enqueue_block_compute(ctx, b, k, x_cur, d_cur, x, cond, tokens, stream, trace);
     if (st != DLO_OK) return st;
     if (trace && tc.end) {
       DLO_HIP(ctx, hipEventRecord(tc.end, stream));
@@ -602,6 +607,7 @@ extern "C" DLO_API dlo_status dlo_forward(dlo_ctx* ctx, float* x, const float* c
   if (x_cur != x)
     DLO_HIP(ctx, hipMemcpyAsync(x, x_cur, size_t(tokens) * size_t(d_cur) * 4, hipMemcpyDeviceToDevice, stream));
   if (trace) ctx->trace_valid = true;
+  ctx->parity ^= L & 1;
   ++ctx->forwards;
   return DLO_OK;
 }
@@ -666,10 +672,11 @@ extern "C" DLO_API dlo_status dlo_debug_assemble(dlo_ctx* ctx, int32_t block, ui
     return fail(DLO_E_INVAL, "host_out must hold %lld elements", (long long)b.layout.numel);
   DeviceGuard dg(ctx->device);
   if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
-  st = enqueue_staging(ctx, block, false, false);
+  const int k = block & 1;  // either slot: the staging waits until no compute reads it
+  st = enqueue_staging(ctx, block, k, false, false);
   if (st != DLO_OK) return st;
   DLO_HIP(ctx, hipStreamSynchronize(ctx->gather_s));
-  DLO_HIP(ctx, hipMemcpy(host_out, ctx->slot[block & 1], size_t(b.layout.numel) * 2, hipMemcpyDeviceToHost));
+  DLO_HIP(ctx, hipMemcpy(host_out, ctx->slot[k], size_t(b.layout.numel) * 2, hipMemcpyDeviceToHost));
   return DLO_OK;
 }
 

@@ -22,7 +22,9 @@ compute), each a mapping with keys:
 
 Properties (each violation is reported as a string):
 
- (i)   block b uses slot b mod 2;
+ (i)   consecutive blocks alternate slots: block b uses slot (b + s0) mod 2,
+       s0 the slot of block 0 (one forward may start in either slot, so that
+       a forward with an odd block count hands its free slot to the next);
  (ii)  compute(b) starts after every reconstruction chunk of b has ended,
        and reconstruction chunk j of b starts after H2D chunk j of b ended;
  (iii) the first reconstruction write into slot(b) starts after compute(b-2)
@@ -83,9 +85,12 @@ def check_trace(trace: Sequence[Mapping], num_blocks: int,
     if errs:
         return errs
 
-    # (i) slot assignment
+    # (i) slot assignment: alternation from block 0's slot
+    s0 = comp[0]["slot"]
+    if s0 not in (0, 1):
+        errs.append(f"(i) block 0 uses slot {s0}")
     for r in list(by_kind["asm"]) + list(by_kind["compute"]):
-        if r["slot"] != r["block"] % 2:
+        if r["slot"] != (r["block"] + s0) % 2:
             errs.append(f"(i) block {r['block']} {r['kind']} uses slot {r['slot']}")
 
     # (ii) ordering inside a block
@@ -108,7 +113,7 @@ def check_trace(trace: Sequence[Mapping], num_blocks: int,
     for b in range(2, num_blocks):
         first = min(r["start"] for r in asm[b])
         if first + slack_ms < comp[b - 2]["end"]:
-            errs.append(f"(iii) block {b} writes slot {b % 2} at {first:.6f} before "
+            errs.append(f"(iii) block {b} writes slot {(b + s0) % 2} at {first:.6f} before "
                         f"compute({b - 2}) ends at {comp[b - 2]['end']:.6f}")
 
     # (iv) residency: at most two blocks in slots, one chunk per landing buffer

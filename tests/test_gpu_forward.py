@@ -239,6 +239,32 @@ def test_trace_two_slot_schedule_image():
     print("stats", st)
 
 
+def test_odd_block_count_alternates_slots_across_forwards():
+    # 3 blocks: block 0 of each forward takes the slot the previous forward's
+    # last block does not use, so consecutive forwards start in slots 0, 1, 0
+    wl = synth.workload("tiny")
+    shapes = list(wl.blocks[:3])
+    W = _weights(wl, range(3))
+    ctx = _ctx(shapes, 4, wl.tokens, flags=dlo.FLAG_TRACE)
+    for b in range(3):
+        ctx.load_shards(b, W[b])
+    x = synth.activations(wl.tokens, 256)
+    cond = synth.conditioning(256)
+    outs = []
+    for step in range(3):
+        outs.append(_run(ctx, x, cond))
+        tr = ctx.trace()
+        assert OT.check_trace(tr, 3) == []
+        first = {r["slot"] for r in tr if r["block"] == 0 and r["kind"] in ("asm", "compute")}
+        assert first == {step % 2}, (step, first)
+    fresh = _ctx(shapes, 4, wl.tokens)
+    for b in range(3):
+        fresh.load_shards(b, W[b])
+    ref = _run(fresh, x, cond)
+    for o in outs:
+        assert np.array_equal(o, ref)
+
+
 # ------------------------------------------------------------------ errors
 
 def test_errors_fail_closed():

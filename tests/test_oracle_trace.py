@@ -7,7 +7,7 @@ import pytest
 from oracle import trace as T
 
 
-def _simulate(n_blocks=6, chunks=3, h2d=1.0, asm=0.2, comp=2.5, serialize=False):
+def _simulate(n_blocks=6, chunks=3, h2d=1.0, asm=0.2, comp=2.5, serialize=False, first_slot=0):
     """Event-driven model of the pipeline: one copy engine, one gather
     stream, one compute stream, two slots, two landing buffers."""
     tr = []
@@ -16,7 +16,7 @@ def _simulate(n_blocks=6, chunks=3, h2d=1.0, asm=0.2, comp=2.5, serialize=False)
     comp_end = {}
     j_global = 0
     for b in range(n_blocks):
-        slot = b % 2
+        slot = (b + first_slot) % 2
         slot_ready = comp_end.get(b - 2, 0.0)
         if serialize:
             slot_ready = max(slot_ready, comp_end.get(b - 1, 0.0))
@@ -113,3 +113,17 @@ def test_capacity_checked():
     tr = _simulate()
     assert T.slot_capacity_elems(NUMELS, 4) == 4 * 251
     assert any(e.startswith("(v)") for e in T.check_trace(tr, 6, slot_capacity=1003, numels=NUMELS, dp=4))
+
+
+def test_forward_may_start_in_slot_one():
+    # a forward that follows one with an odd block count starts in slot 1
+    tr = _simulate(first_slot=1)
+    assert T.check_trace(tr, 6, slot_capacity=4 * 251, numels=NUMELS, dp=4) == []
+
+
+def test_broken_alternation_caught_from_either_start():
+    for first in (0, 1):
+        tr = _simulate(first_slot=first)
+        _find(tr, "asm", 2)["slot"] = (2 + first + 1) % 2
+        errs = T.check_trace(tr, 6)
+        assert any(e.startswith("(i)") for e in errs), errs
