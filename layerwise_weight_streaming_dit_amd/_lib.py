@@ -105,6 +105,10 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m layerwise_weight_streaming_dit_amd.build`")
+        # PyTorch brings its own HIP runtime; loading it first makes the
+        # library bind to that same runtime (one runtime per process) instead
+        # of loading the system copy next to it.
+        import torch  # noqa: F401
         l = ctypes.CDLL(LIB_PATH)
         for name, args in _SIGNATURES.items():
             f = getattr(l, name)
