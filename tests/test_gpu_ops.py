@@ -201,6 +201,16 @@ def test_attention(T, H, hd):
     assert ok, (ma, mr)
 
 
+@pytest.mark.parametrize("T", [65, 1000])
+@pytest.mark.parametrize("H,hd", [(8, 64), (16, 128)])
+def test_attention_heads_per_xcd(T, H, hd):
+    # head counts divisible by 8 take the grid mapping that keeps each head's
+    # query tiles on one XCD
+    got, want = _attention_case(T, H, hd, seed=T + H)
+    ok, ma, mr = within(got, want, rtol=5e-3, atol=5e-3)
+    assert ok, (ma, mr)
+
+
 @pytest.mark.parametrize("qscale", [4.0, 30.0])
 def test_attention_peaked_softmax(qscale):
     got, want = _attention_case(300, 2, 128, qscale=qscale, seed=7)
