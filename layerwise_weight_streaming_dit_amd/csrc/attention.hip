@@ -53,7 +53,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(
     const uint16_t* __restrict__ qk, int ld_qk, const uint16_t* __restrict__ vt, int ld_vt,
     uint16_t* __restrict__ o, int ld_o, int T, int H, float scale_log2) {
   constexpr int KCH = HD / 8;           // 16-byte chunks per K row
-  constexpr int KSWZ = (KCH >= 16) ? 15 : 7;
+  // 16-byte chunk swizzles, so that the 16 lanes the LDS serves together
+  // (16 consecutive rows, same logical chunk) hit 16 distinct 16-byte bank
+  // groups of the 256-byte bank row: 256-byte rows (K, hd 128) XOR the chunk
+  // with row % 16; 128-byte rows (V^T, and K for hd 64) pair rows r and r + 8
+  // in the same half of a bank row, so they also XOR with row / 8.
+  auto swz = [](int row, int nch) { return nch >= 16 ? (row & 15) : ((row ^ (row >> 3)) & 7); };
   constexpr int NK = kBKV * KCH / kAttnThreads;  // K chunks per thread per step
   constexpr int NV = HD * 8 / kAttnThreads;      // V^T chunks per thread per step
   constexpr int NKK = HD / 16;                    // MFMA k-steps over the head dim
@@ -100,13 +105,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(
     const int q = tid + i * kAttnThreads, j = q / KCH, c = q % KCH;
     k_row[i] = j;
     k_chunk[i] = c;
-    k_lds[i] = j * HD + ((c ^ (j & KSWZ)) << 3);
+    k_lds[i] = j * HD + ((c ^ swz(j, KCH)) << 3);
   }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int q = tid + i * kAttnThreads, row = q >> 3, c = q & 7;
     v_src[i] = vt + (static_cast<int64_t>(h) * HD + row) * ld_vt + c * 8;
-    v_lds[i] = row * kBKV + ((c ^ (row & 7)) << 3);
+    v_lds[i] = row * kBKV + ((c ^ swz(row, 8)) << 3);
   }
 
   u32x4_t rk[NK], rv[NV];
@@ -146,7 +151,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         const int c = kk * 2 + g;
-        const f16x8_t a = *reinterpret_cast<const f16x8_t*>(&sK[cur][krow * HD + ((c ^ (krow & KSWZ)) << 3)]);
+        const f16x8_t a = *reinterpret_cast<const f16x8_t*>(&sK[cur][krow * HD + ((c ^ swz(krow, KCH)) << 3)]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[kk], s[kb], 0, 0, 0);
       }
     }
@@ -199,7 +204,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int c = kb * 4 + ks * 2 + g;
-          const f16x8_t a = *reinterpret_cast<const f16x8_t*>(&sV[cur][vrow * kBKV + ((c ^ (vrow & 7)) << 3)]);
+          const f16x8_t a = *reinterpret_cast<const f16x8_t*>(&sV[cur][vrow * kBKV + ((c ^ swz(vrow, 8)) << 3)]);
           oacc[ib] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, pb[kb][ks], oacc[ib], 0, 0, 0);
         }
     }
