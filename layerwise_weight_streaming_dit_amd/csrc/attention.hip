@@ -29,9 +29,10 @@
 // and the final division by the running sum is unchanged, so the result is
 // the same softmax.  Key masking runs only in the last, partial tile.
 //
-// Tiles: 128 queries (4 waves) per workgroup, 64 keys per step, K and V^T
-// double-buffered in LDS with XOR-swizzled 16-byte chunks; the next tile's
-// global loads are issued before the current tile's MFMAs.
+// Tiles: 256 queries (8 waves, two per SIMD) per workgroup and one workgroup
+// per CU, so each K/V tile fetched from L2 feeds 256 queries; 64 keys per
+// step, K and V^T double-buffered in LDS with XOR-swizzled 16-byte chunks; the
+// next tile's global loads are issued before the current tile's MFMAs.
 #include <math.h>
 
 #include <type_traits>
@@ -43,13 +44,13 @@ namespace dlo {
 
 namespace {
 
-constexpr int kAttnThreads = 256;
-constexpr int kBQ = 128;           // queries per workgroup (32 per wave)
+constexpr int kAttnThreads = 512;
+constexpr int kBQ = 256;           // queries per workgroup (32 per wave)
 constexpr int kBKV = 64;           // keys per step
 constexpr float kRescaleSlack = 8.0f;  // log2 of the largest unnormalised probability
 
 template <int HD>
-__global__ __launch_bounds__(kAttnThreads, 2) void attention_kernel(
+__global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(
     const uint16_t* __restrict__ qk, int ld_qk, const uint16_t* __restrict__ vt, int ld_vt,
     uint16_t* __restrict__ o, int ld_o, int T, int H, float scale_log2) {
   constexpr int KCH = HD / 8;           // 16-byte chunks per K row
