@@ -125,6 +125,31 @@ def test_tiny_ragged_tokens(T):
     assert ok, (T, ma, mr)
 
 
+def test_smallest_block_with_all_padding_shards():
+    # the smallest block the kernels accept (d 128, hd 64, MLP 128, cond 64)
+    # has 148992 elements; at dp 1024 the shard size is 146 and the last three
+    # shards hold only padding (degenerate shards of the ceil-division rule)
+    shp = synth.BlockShape(128, 2, 128, 64)
+    numel = OL.block_numel(shp)
+    dp = 1024
+    S = OS.shard_size(numel, dp)
+    assert (dp - 1) * S >= numel  # at least one all-padding shard
+    rng = np.random.default_rng(5)
+    flat = synth.bf16_bits_from_f32((rng.standard_normal(numel) * 0.02).astype(np.float32))
+    ctx = _ctx([shp, shp], dp, 64)
+    ctx.load_shards(0, flat)
+    ctx.load_shards(1, flat[::-1].copy())
+    for r in (0, dp - 1):
+        assert np.array_equal(ctx.get_shard(0, r), OS.shard(flat, dp)[r])
+    assert np.array_equal(ctx.debug_assemble(0), flat)
+    x = synth.activations(64, 128)
+    cond = synth.conditioning(64)
+    got = _run(ctx, x, cond)
+    want = D.dit_forward([flat, flat[::-1].copy()], [shp, shp], x, cond)
+    ok, ma, mr = within(got, want)
+    assert ok, (ma, mr)
+
+
 def _sampled_block_check(wl, b, T, dp, rows=48):
     shp = wl.blocks[b]
     flat = synth.block_weights(wl.wid, b, OL.block_numel(shp))
