@@ -77,14 +77,20 @@ def host_info():
 
 
 def source_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """sha256[:16] of a kernel source together with the device headers it
+    includes (a change to either invalidates counters taken on the kernel)."""
+    h = hashlib.sha256(open(path, "rb").read())
+    d = os.path.dirname(path)
+    for inc in ("device_common.h", "kernels.h"):
+        h.update(open(os.path.join(d, inc), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(kernel_src, kind):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter
     summary (profiles/hbm_traffic_image_dit.txt: lines "kind source-sha16
     fetch-bytes write-bytes", copy-calibrated), used only if the summary was
-    taken on the current kernel source; else None."""
+    taken on the current kernel source and device headers; else None."""
     p = os.path.join(ROOT, "profiles", "hbm_traffic_image_dit.txt")
     if not os.path.exists(p):
         return None

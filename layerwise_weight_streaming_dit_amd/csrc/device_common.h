@@ -49,17 +49,22 @@ __device__ __forceinline__ int vt_key_position(int j) {
   return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
 }
 
-// tanh-approximated GELU: 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))),
-// with tanh(y) = 1 - 2 / (exp(2y) + 1).
+// tanh-approximated GELU: 0.5 z (1 + tanh(y)), y = sqrt(2/pi) (z + 0.044715 z^3).
+// Since 0.5 (1 + tanh(y)) = 1 / (1 + exp(-2y)), this is z / (1 + 2^(-2y log2 e)):
+// one exp2 and one reciprocal (v_exp_f32, v_rcp_f32, about 1 ulp each) instead
+// of an IEEE division.  Large |z| saturate correctly (exp2 -> inf gives -0,
+// exp2 -> 0 gives z).
 __device__ __forceinline__ float gelu_tanh(float z) {
-  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-  const float k1 = 0.044715f;
-  float y = k0 * (z + k1 * z * z * z);
-  float t = 1.0f - 2.0f / (__expf(2.0f * y) + 1.0f);
-  return 0.5f * z * (1.0f + t);
+  const float c0 = 2.0f * 0.7978845608028654f * 1.4426950408889634f;  // 2 sqrt(2/pi) log2(e)
+  const float c1 = c0 * 0.044715f;
+  const float t = z * fmaf(c1, z * z, c0);  // 2 y log2(e)
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t));
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU z / (1 + exp(-z)) with exp2 and a reciprocal (see gelu_tanh).
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
 
 // Wave-wide (64 lanes) reductions.
 __device__ __forceinline__ float wave_sum(float v) {
