@@ -279,6 +279,23 @@ def main():
     asm_read = sum(r["bytes"] for r in by.get("asm", []))
     overlap_E = max(h2d_ms + asm_ms, comp_ms) / t_fwd
     hidden = (h2d_ms + comp_ms - t_fwd) / min(h2d_ms, comp_ms)
+    # steady state: the staging of blocks 1..L-1 against the compute of
+    # blocks 0..L-2 (what can overlap once the pipeline is full), inside the
+    # window from the first staging of block 1 to the end of compute(L-2)
+    steady = None
+    if L >= 3:
+        st_rs = [r for r in tr if r["kind"] in ("h2d", "asm") and r["block"] >= 1]
+        cp_rs = [r for r in tr if r["kind"] == "compute" and r["block"] <= L - 2]
+        w0 = min(r["start"] for r in st_rs if r["block"] == 1)
+        w1 = max(r["end"] for r in cp_rs if r["block"] == L - 2)
+        clip = lambda rs: [dict(r, start=max(r["start"], w0), end=min(r["end"], w1)) for r in rs
+                           if r["end"] > w0 and r["start"] < w1]
+        h_s = busy(clip([r for r in st_rs if r["kind"] == "h2d"]))
+        a_s = busy(clip([r for r in st_rs if r["kind"] == "asm"]))
+        c_s = busy(clip(cp_rs))
+        win = w1 - w0
+        steady = {"window_ms": win, "sum_h2d_ms": h_s, "sum_asm_ms": a_s, "sum_compute_ms": c_s,
+                  "E": max(h_s + a_s, c_s) / win, "hidden_frac": (h_s + c_s - win) / min(h_s, c_s)}
     kernels = {}
     for kind in KERNEL_KINDS:
         rs = by.get(kind, [])
@@ -386,7 +403,8 @@ def main():
                           "host_enqueue_note": "timed context records HIP events around every kernel",
                           "host_enqueue_us_per_forward_untraced": enqueue_untraced_us},
         "overlap": {"E": overlap_E, "hidden_frac": hidden, "t_forward_ms": t_fwd, "sum_h2d_ms": h2d_ms,
-                    "sum_asm_ms": asm_ms, "sum_compute_ms": comp_ms, "serialized_ms": serial},
+                    "sum_asm_ms": asm_ms, "sum_compute_ms": comp_ms, "serialized_ms": serial,
+                    "steady_state": steady},
         "residency": {"high_water_blocks": st["residency_high_water"], "slot_bytes": st["slot_bytes"],
                       "landing_bytes": st["landing_bytes"], "workspace_bytes": st["workspace_bytes"]},
         "kernels": kernels,
