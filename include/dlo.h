@@ -117,8 +117,12 @@ typedef struct dlo_config {
   int32_t dp_size;             /* number of shards per block, >= 1 */
   int32_t max_tokens;          /* largest token count dlo_forward accepts, in [1, 2^20], and
                                   max_tokens * max(d_model, d_mlp) * 2 bytes below 4 GiB */
-  int64_t landing_chunk_elems; /* H2D chunk size in elements; 0 = default
-                                  min(max shard size, 2^24); else >= 4096 */
+  int64_t landing_chunk_elems; /* largest H2D chunk in elements; 0 = default
+                                  min(dp * max shard size, 2^26); else >= 4096.
+                                  A block's padded weight is split into equal
+                                  chunks of at most this size (they may span
+                                  shards, which sit back to back in one pinned
+                                  region per block) */
   int32_t device;              /* HIP device ordinal the context runs on */
   uint32_t flags;              /* DLO_FLAG_* */
   void* arena;                 /* device memory owned by the caller, 256-byte
@@ -209,7 +213,8 @@ DLO_API dlo_status dlo_create(const dlo_config* cfg, dlo_ctx** out);
 
 /* Shard and pin one block: numel must equal the block's layout numel
  * (else DLO_E_SHAPE).  Allocates dp_size pinned host shards of
- * ceil(numel / dp_size) elements, copies the flat weight's slice into each and
+ * S = ceil(numel / dp_size) elements (back to back in one pinned region:
+ * shard r at element r * S), copies the flat weight's slice into each and
  * zero-pads the tail.  Keeps no reference to flat_bf16: the caller may free it
  * on return.  Reloading a block replaces its shards; waits for in-flight work
  * on the context's streams first. */

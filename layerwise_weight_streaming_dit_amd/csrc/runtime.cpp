@@ -51,16 +51,21 @@ namespace dlo {
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int64_t kDefaultChunk = int64_t(1) << 24;
+// Default H2D chunk (128 MB): larger transfers run closer to the pinned
+// link's rate (image-shape forward: 55.3 / 54.5 / 53.7 / 53.5 ms with 16 / 32
+// / 64 / 128 MB chunks, against 52.6 ms for back-to-back raw copies).
+constexpr int64_t kDefaultChunk = int64_t(1) << 26;
 constexpr int64_t kMinChunk = 4096;
 constexpr int kLandSlack = 8;  // landing offset (elements) used to co-align with the slot
 
+// One H2D transfer.  The dp shards of a block sit back to back in one pinned
+// region (shard r at element r * S), so their concatenation -- the gather's
+// output, the flat weight followed by the zero padding -- is contiguous, and a
+// chunk is a range of it that may span several shards.
 struct Chunk {
-  int32_t rank;
-  int64_t src_off;   // element offset inside the shard
-  int64_t len;       // elements copied host -> device
-  int64_t dst;       // element offset inside the slot (rank * S + src_off)
-  int64_t valid;     // elements reconstructed (padding dropped)
+  int64_t off;    // element offset in the concatenation = offset in the slot
+  int64_t len;    // elements copied host -> device
+  int64_t valid;  // elements reconstructed (the trailing padding is dropped)
 };
 
 struct Block {
@@ -68,7 +73,8 @@ struct Block {
   std::vector<int64_t> extra;
   BlockLayout layout;
   int64_t shard = 0;  // S_b
-  std::vector<uint16_t*> shards;  // dp pinned buffers, empty until loaded
+  uint16_t* pinned = nullptr;     // dp * S_b pinned elements, null until loaded
+  std::vector<uint16_t*> shards;  // shard r = pinned + r * S_b
   std::vector<Chunk> chunks;
 };
 
@@ -198,8 +204,10 @@ dlo_status compute_sizes(const dlo_config* cfg, Sizes* z) {
   if (size_t(cfg->max_tokens) * size_t(std::max(z->d_max, z->m_max)) * 2 > size_t(UINT32_MAX))
     return fail(DLO_E_INVAL, "max_tokens %d too large for the widest block (activations beyond 4 GiB)",
                 cfg->max_tokens);
-  z->chunk = cfg->landing_chunk_elems ? cfg->landing_chunk_elems : std::min<int64_t>(z->s_max, kDefaultChunk);
-  z->chunk = std::min<int64_t>(z->chunk, z->s_max);
+  // largest padded block, dp * S_max elements: no chunk needs to be longer
+  const int64_t padded_max = int64_t(cfg->dp_size) * z->s_max;
+  z->chunk = cfg->landing_chunk_elems ? cfg->landing_chunk_elems : std::min<int64_t>(padded_max, kDefaultChunk);
+  z->chunk = std::min<int64_t>(z->chunk, padded_max);
   z->slot_bytes = align_up(size_t(2) * size_t(cfg->dp_size) * size_t(z->s_max), kAlign);
   z->landing_bytes = 2 * align_up(size_t(2) * size_t(z->chunk + kLandSlack), kAlign);
   const size_t T = size_t(cfg->max_tokens), Tp = align_up(T, 64);
@@ -219,17 +227,16 @@ dlo_status compute_sizes(const dlo_config* cfg, Sizes* z) {
 
 void build_chunks(Block& b, int dp, int64_t chunk) {
   b.chunks.clear();
-  const int64_t S = b.shard, n = b.layout.numel;
-  for (int r = 0; r < dp; ++r) {
-    for (int64_t off = 0; off < S; off += chunk) {
-      Chunk c;
-      c.rank = r;
-      c.src_off = off;
-      c.len = std::min(chunk, S - off);
-      c.dst = int64_t(r) * S + off;
-      c.valid = std::max<int64_t>(0, std::min(c.len, n - c.dst));
-      b.chunks.push_back(c);
-    }
+  const int64_t total = int64_t(dp) * b.shard, n = b.layout.numel;
+  // equal chunks (multiples of 8 elements) of at most `chunk` elements
+  const int64_t nch = std::max<int64_t>(1, (total + chunk - 1) / chunk);
+  const int64_t len = std::min(chunk, ((total + nch - 1) / nch + 7) / 8 * 8);
+  for (int64_t off = 0; off < total; off += len) {
+    Chunk c;
+    c.off = off;
+    c.len = std::min(len, total - off);
+    c.valid = std::max<int64_t>(0, std::min(c.len, n - off));
+    b.chunks.push_back(c);
   }
 }
 
@@ -247,7 +254,7 @@ dlo_status enqueue_staging(dlo_ctx* ctx, int b, int k, bool trace, bool in_forwa
     const Chunk& c = blk.chunks[ci];
     const int lb = static_cast<int>(ctx->land_counter & 1);
     ++ctx->land_counter;
-    const int64_t co = c.dst % kLandSlack;  // co-align landing with slot (mod 16 bytes)
+    const int64_t co = c.off % kLandSlack;  // co-align landing with slot (mod 16 bytes)
     uint16_t* land = ctx->landing[lb] + co;
     hipStream_t cs = lb ? ctx->copy_s2 : ctx->copy_s;
     // copy stream of this landing buffer
@@ -261,8 +268,7 @@ dlo_status enqueue_staging(dlo_ctx* ctx, int b, int k, bool trace, bool in_forwa
       tv = TraceEv{DLO_IV_H2D, b, static_cast<int>(ci), -1, lb, c.len * 2, next_ev(ctx), next_ev(ctx)};
       if (tv.start) DLO_HIP(ctx, hipEventRecord(tv.start, cs));
     }
-    DLO_HIP(ctx, hipMemcpyAsync(land, blk.shards[c.rank] + c.src_off, size_t(c.len) * 2,
-                                hipMemcpyHostToDevice, cs));
+    DLO_HIP(ctx, hipMemcpyAsync(land, blk.pinned + c.off, size_t(c.len) * 2, hipMemcpyHostToDevice, cs));
     if (trace && tv.end) {
       DLO_HIP(ctx, hipEventRecord(tv.end, cs));
       ctx->trace.push_back(tv);
@@ -280,7 +286,7 @@ dlo_status enqueue_staging(dlo_ctx* ctx, int b, int k, bool trace, bool in_forwa
       ta = TraceEv{DLO_IV_ASM, b, static_cast<int>(ci), k, lb, c.valid * 2, next_ev(ctx), next_ev(ctx)};
       if (ta.start) DLO_HIP(ctx, hipEventRecord(ta.start, ctx->gather_s));
     }
-    DLO_HIP(ctx, launch_assemble(ctx->slot[k] + c.dst, land, c.valid, ctx->gather_s));
+    DLO_HIP(ctx, launch_assemble(ctx->slot[k] + c.off, land, c.valid, ctx->gather_s));
     if (trace && ta.end) {
       DLO_HIP(ctx, hipEventRecord(ta.end, ctx->gather_s));
       ctx->trace.push_back(ta);
@@ -379,8 +385,7 @@ dlo_status sync_ctx(dlo_ctx* ctx) {
 
 void free_ctx(dlo_ctx* ctx) {
   for (auto& b : ctx->blocks)
-    for (auto* p : b.shards)
-      if (p) (void)hipHostFree(p);
+    if (b.pinned) (void)hipHostFree(b.pinned);
   for (auto e : ctx->ev_pool) (void)hipEventDestroy(e);
   if (ctx->created_events) {
     for (int i = 0; i < 2; ++i) {
@@ -532,24 +537,17 @@ extern "C" DLO_API dlo_status dlo_load_shards(dlo_ctx* ctx, int32_t block, const
   DLO_HIP(ctx, hipStreamSynchronize(ctx->copy_s));
   DLO_HIP(ctx, hipStreamSynchronize(ctx->copy_s2));
   const int64_t S = b.shard;
-  if (b.shards.empty()) {
-    b.shards.assign(ctx->dp, nullptr);
-    for (int r = 0; r < ctx->dp; ++r) {
-      void* p = nullptr;
-      hipError_t e = hipHostMalloc(&p, size_t(std::max<int64_t>(S, 1)) * 2, hipHostMallocDefault);
-      if (e != hipSuccess || p == nullptr) {
-        for (auto*& q : b.shards)
-          if (q) {
-            (void)hipHostFree(q);
-            q = nullptr;
-          }
-        b.shards.clear();
-        (void)hipGetLastError();
-        return fail(DLO_E_HOST_OOM, "block %d: pinned allocation of %lld bytes failed", block,
-                    (long long)(S * 2));
-      }
-      b.shards[r] = static_cast<uint16_t*>(p);
+  if (b.pinned == nullptr) {
+    void* p = nullptr;
+    const size_t bytes = size_t(std::max<int64_t>(int64_t(ctx->dp) * S, 1)) * 2;
+    hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocDefault);
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return fail(DLO_E_HOST_OOM, "block %d: pinned allocation of %zu bytes failed", block, bytes);
     }
+    b.pinned = static_cast<uint16_t*>(p);
+    b.shards.assign(ctx->dp, nullptr);
+    for (int r = 0; r < ctx->dp; ++r) b.shards[r] = b.pinned + int64_t(r) * S;
   }
   for (int r = 0; r < ctx->dp; ++r) {
     const int64_t lo = int64_t(r) * S;

@@ -58,8 +58,8 @@ def test_required_bytes_two_slots_of_largest_block(name):
         one_slot_aligned = -(-one_slot // 256) * 256
         assert sz["slots"] == 2 * one_slot_aligned
         assert sz["total"] >= sz["slots"] + sz["landing"] + sz["workspace"]
-        # landing: two chunks of at most 2^24 elements (+ co-alignment slack)
-        assert sz["landing"] <= 2 * (-(-((1 << 24) + 8) * 2 // 256) * 256)
+        # landing: two chunks of at most 2^26 elements (+ co-alignment slack)
+        assert sz["landing"] <= 2 * (-(-((1 << 26) + 8) * 2 // 256) * 256)
 
 
 def _cfg(shapes, **kw):
