@@ -39,6 +39,7 @@
 
 #include <algorithm>
 #include <memory>
+#include <thread>
 #include <vector>
 
 #include <hip/hip_runtime.h>
@@ -223,6 +224,26 @@ dlo_status compute_sizes(const dlo_config* cfg, Sizes* z) {
   z->workspace_bytes = ws;
   z->total = 2 * z->slot_bytes + z->landing_bytes + z->workspace_bytes;
   return DLO_OK;
+}
+
+// memcpy split over a few threads (large blocks are GBs; one thread copies
+// at a fraction of the host's memory bandwidth).
+void copy_parallel(void* dst, const void* src, size_t bytes) {
+  constexpr size_t kPiece = size_t(64) << 20;
+  const size_t hw = std::max(1u, std::thread::hardware_concurrency());
+  const size_t nt = std::min<size_t>({8, hw, (bytes + kPiece - 1) / kPiece});
+  if (nt <= 1) {
+    if (bytes) memcpy(dst, src, bytes);
+    return;
+  }
+  const size_t per = (bytes + nt - 1) / nt;
+  std::vector<std::thread> pool;
+  for (size_t t = 1; t < nt; ++t) {
+    const size_t lo = t * per, n = lo < bytes ? std::min(per, bytes - lo) : 0;
+    if (n) pool.emplace_back([=] { memcpy(static_cast<char*>(dst) + lo, static_cast<const char*>(src) + lo, n); });
+  }
+  memcpy(dst, src, std::min(per, bytes));
+  for (auto& th : pool) th.join();
 }
 
 void build_chunks(Block& b, int dp, int64_t chunk) {
@@ -549,12 +570,10 @@ extern "C" DLO_API dlo_status dlo_load_shards(dlo_ctx* ctx, int32_t block, const
     b.shards.assign(ctx->dp, nullptr);
     for (int r = 0; r < ctx->dp; ++r) b.shards[r] = b.pinned + int64_t(r) * S;
   }
-  for (int r = 0; r < ctx->dp; ++r) {
-    const int64_t lo = int64_t(r) * S;
-    const int64_t n = std::max<int64_t>(0, std::min(S, numel - lo));
-    if (n > 0) memcpy(b.shards[r], flat + lo, size_t(n) * 2);
-    if (n < S) memset(b.shards[r] + n, 0, size_t(S - n) * 2);
-  }
+  // shard r = flat[r S, min((r + 1) S, numel)) then zeros: with the shards
+  // back to back this is the flat weight followed by the zero padding
+  copy_parallel(b.pinned, flat, size_t(numel) * 2);
+  memset(b.pinned + numel, 0, (size_t(ctx->dp) * size_t(S) - size_t(numel)) * 2);
   return DLO_OK;
 }
 
