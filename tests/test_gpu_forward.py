@@ -185,6 +185,26 @@ def _tiny_out(dp=4, flags=0, chunk=0, W=None, x=None):
     return out, ctx
 
 
+def test_image_chained_forward_sampled_rows():
+    # the whole 28-block image forward (weights streamed through both slots
+    # 14 times) against the oracle's chained fp64 forward on sampled rows
+    # (tests/golden/image_chain_rows.npz, written by make_image_chain.py)
+    import os
+    z = np.load(os.path.join(os.path.dirname(__file__), "golden", "image_chain_rows.npz"))
+    wl = synth.workload("image")
+    shapes = list(wl.blocks)
+    numels = [OL.block_numel(s) for s in shapes]
+    W = synth.many_block_weights(wl.wid, numels)
+    ctx = _ctx(shapes, 4, wl.tokens)
+    for b in range(len(shapes)):
+        ctx.load_shards(b, W[b])
+    got = _run(ctx, synth.activations(wl.tokens, 2048), synth.conditioning(256))
+    ctx.close()
+    ok, ma, mr = within(got[z["rows"]], z["out"])
+    print(f"image chained 28 blocks: max_abs {ma:.3e} max_rel {mr:.3e}")
+    assert ok, (ma, mr)
+
+
 def test_outputs_identical_across_dp_chunking_and_schedule():
     base, _ = _tiny_out()
     for dp in (1, 3, 8):
