@@ -39,6 +39,64 @@ __global__ __launch_bounds__(kNormThreads) void adaln_kernel(const uint16_t* __r
   }
 }
 
+// One wave per token row, four rows per workgroup: the row (adapted to width
+// d) is held in registers, NV float4 per lane (NV * 256 >= d), so mean and
+// variance are wave reductions with no LDS or barrier, and every lane has NV
+// loads in flight.  The register cap keeps 4 waves per SIMD resident for
+// d <= 2048, 2 up to 4096; wider rows use the workgroup-per-row kernel below.
+template <int NV>
+__global__ __launch_bounds__(256, NV <= 8 ? 4 : 2) void ln_modulate_kernel(
+    const float* __restrict__ xin, int d_in, float* __restrict__ xout, const float* __restrict__ shift,
+    const float* __restrict__ scale, uint16_t* __restrict__ h, int tokens, int d) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= tokens) return;
+  const float* xr = xin + t * d_in;
+  const int nv = d / 4;
+  const int lim = min(nv, d_in / 4);  // float4s of the row that come from xin
+  f32x4_t v[NV];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    // every lane loads (clamped in bounds) and zeroes what lies past the
+    // input row: no divergent branch around the loads
+    const int q = lane + i * 64;
+    const f32x4_t l = *reinterpret_cast<const f32x4_t*>(xr + min(q, lim - 1) * 4);
+    const bool in = q < lim;
+    v[i] = f32x4_t{in ? l.x : 0.f, in ? l.y : 0.f, in ? l.z : 0.f, in ? l.w : 0.f};
+    s += v[i].x + v[i].y + v[i].z + v[i].w;
+  }
+  const float mean = wave_sum(s) / static_cast<float>(d);
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int q = lane + i * 64;
+    if (q < nv) {
+      const f32x4_t e = v[i] - mean;
+      ss += e.x * e.x + e.y * e.y + e.z * e.z + e.w * e.w;
+    }
+  }
+  const float var = wave_sum(ss) / static_cast<float>(d);
+  const float rstd = rsqrtf(var + 1e-6f);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int q = lane + i * 64;
+    // one float4 at a time: hoisting every shift/scale load would double
+    // the live registers
+    __builtin_amdgcn_sched_barrier(0);
+    if (q < nv) {
+      const f32x4_t sh = *reinterpret_cast<const f32x4_t*>(shift + q * 4);
+      const f32x4_t sc = *reinterpret_cast<const f32x4_t*>(scale + q * 4);
+      const f32x4_t y = (v[i] - mean) * rstd * (1.0f + sc) + sh;
+      u32x2_t o;
+      o.x = pack_f16x2(y.x, y.y);
+      o.y = pack_f16x2(y.z, y.w);
+      *reinterpret_cast<u32x2_t*>(h + t * d + q * 4) = o;
+      if (xout != nullptr) *reinterpret_cast<f32x4_t*>(xout + t * d + q * 4) = v[i];
+    }
+  }
+}
+
 template <int THREADS>
 __device__ __forceinline__ float block_sum(float v, float* red) {
   v = wave_sum(v);
@@ -52,12 +110,12 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
-// One workgroup per token row.  The row (adapted to width d) is held in
-// registers, at most two float4 per thread (the workgroup grows with d, up to
-// 1024 threads for d = 8192, so registers stay few and occupancy high); mean
-// and variance are two passes over the registers.
+// Wide rows (d > 4096): one workgroup per token row.  The row (adapted to
+// width d) is held in registers, at most two float4 per thread (1024 threads
+// for d = 8192, so registers stay few and occupancy high); mean and variance
+// are workgroup reductions over the registers.
 template <int THREADS, int NV>
-__global__ __launch_bounds__(THREADS) void ln_modulate_kernel(
+__global__ __launch_bounds__(THREADS) void ln_modulate_row_kernel(
     const float* __restrict__ xin, int d_in, float* __restrict__ xout, const float* __restrict__ shift,
     const float* __restrict__ scale, uint16_t* __restrict__ h, int d) {
   __shared__ float red[THREADS / 64];
@@ -114,15 +172,18 @@ hipError_t launch_adaln(const uint16_t* w, const uint16_t* b, const float* cond,
 hipError_t launch_ln_modulate(const float* xin, int d_in, float* xout, const float* shift,
                               const float* scale, uint16_t* h, int tokens, int d, hipStream_t s) {
   if (tokens <= 0) return hipSuccess;
-  const dim3 grid(tokens);
-  if (d <= 1024)
-    hipLaunchKernelGGL((ln_modulate_kernel<256, 1>), grid, dim3(256), 0, s, xin, d_in, xout, shift, scale, h, d);
-  else if (d <= 2048)
-    hipLaunchKernelGGL((ln_modulate_kernel<256, 2>), grid, dim3(256), 0, s, xin, d_in, xout, shift, scale, h, d);
-  else if (d <= 4096)
-    hipLaunchKernelGGL((ln_modulate_kernel<512, 2>), grid, dim3(512), 0, s, xin, d_in, xout, shift, scale, h, d);
+  const dim3 grid((tokens + 3) / 4), block(256);
+#define DLO_LN(NV) \
+  hipLaunchKernelGGL((ln_modulate_kernel<NV>), grid, block, 0, s, xin, d_in, xout, shift, scale, h, tokens, d)
+  if (d <= 256) DLO_LN(1);
+  else if (d <= 512) DLO_LN(2);
+  else if (d <= 1024) DLO_LN(4);
+  else if (d <= 2048) DLO_LN(8);
+  else if (d <= 4096) DLO_LN(16);
   else
-    hipLaunchKernelGGL((ln_modulate_kernel<1024, 2>), grid, dim3(1024), 0, s, xin, d_in, xout, shift, scale, h, d);
+    hipLaunchKernelGGL((ln_modulate_row_kernel<1024, 2>), dim3(tokens), dim3(1024), 0, s, xin, d_in, xout, shift,
+                       scale, h, d);
+#undef DLO_LN
   return hipGetLastError();
 }
 
