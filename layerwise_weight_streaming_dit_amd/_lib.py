@@ -207,6 +207,14 @@ class StreamedDiT:
         """xbuf: cuda fp32 tensor holding tokens * max_d floats whose first
         tokens * d_first are x; returns the [tokens, d_last] view of the
         result.  Asynchronous on `stream` (default: torch's current stream)."""
+        import torch
+        if xbuf.dtype != torch.float32 or not xbuf.is_cuda or not xbuf.is_contiguous():
+            raise ValueError("xbuf must be a contiguous float32 CUDA tensor")
+        if xbuf.numel() < tokens * self.max_d:
+            raise ValueError(f"xbuf holds {xbuf.numel()} floats; tokens * max_d = {tokens * self.max_d}")
+        d_cond = getattr(self.shapes[0], "d_cond", 256)
+        if cond.dtype != torch.float32 or not cond.is_cuda or cond.numel() < d_cond:
+            raise ValueError(f"cond must be a float32 CUDA tensor of {d_cond} elements")
         check(lib().dlo_forward(self._h, xbuf.data_ptr(), cond.data_ptr(), tokens, _stream_handle(stream)))
         d_last = self.shapes[-1].d_model
         return xbuf.view(-1)[: tokens * d_last].view(tokens, d_last)
