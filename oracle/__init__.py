@@ -24,7 +24,8 @@ Contents:
 
 Every function here is pinned by ``tests/test_oracle_*.py`` (closed forms,
 library routines, brute force on tiny inputs, special cases and the pages'
-own figures); the block math beyond those pins is "parity unpinned by the
-pages", since the pages print no numeric example of it.
+own figures).  The pages print no numeric example of the block math, so its
+pins come from the mathematics (closed forms, library routines, special
+cases) rather than from values the pages print.
 """
 from . import layout, shard, dit, trace  # noqa: F401

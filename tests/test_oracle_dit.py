@@ -2,8 +2,8 @@
 forms, the block's composition through special cases that reduce to closed
 form, and a full-block cross-check against PyTorch's fp64 library ops.
 
-The pages print no numeric example of the block math, so past these pins
-the block is "parity unpinned by the pages"."""
+The pages print no numeric example of the block math, so these pins come
+from the mathematics and from library routines, not from page values."""
 import numpy as np
 import pytest
 import scipy.special
