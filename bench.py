@@ -211,6 +211,7 @@ def main():
     for _ in range(args.warmup):
         ctx.forward(xbuf, cond, T)
     torch.cuda.synchronize()
+    ctx.trace()  # kernel intervals accumulate until read: drop the warm-up's
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ts = time.perf_counter()
@@ -229,7 +230,7 @@ def main():
     print(f"[bench] timed {args.steps} forwards: {ms_per_step:.3f} ms/forward (events {ev_ms / args.steps:.3f})",
           file=sys.stderr, flush=True)
 
-    # kernel durations: the last forward of the timed region
+    # kernel durations: every launch of the timed region
     ktr = ctx.trace()
     # one forward on an idle device (no previous forward to overlap its
     # pipeline fill with): the difference to the back-to-back step time is

@@ -92,7 +92,10 @@ typedef int32_t dlo_status;
                                       ahead of the reconstruction shows up */
 #define DLO_FLAG_TRACE_KERNELS 0x8u /* record only the compute-stream intervals
                                        (block compute and each kernel): keeps
-                                       events off the copy and gather streams */
+                                       events off the copy and gather streams.
+                                       Without DLO_FLAG_TRACE the intervals
+                                       accumulate over forwards until
+                                       dlo_get_trace hands them out */
 
 typedef struct dlo_ctx dlo_ctx;
 
@@ -257,8 +260,12 @@ DLO_API dlo_status dlo_debug_assemble(dlo_ctx* ctx, int32_t block, uint16_t* hos
  * context's streams. */
 DLO_API dlo_status dlo_get_stats(dlo_ctx* ctx, dlo_stats* out);
 
-/* The intervals of the last traced forward (cap entries at most; *n receives
- * the number recorded).  Synchronises the context's streams. */
+/* The intervals of the last traced forward (DLO_FLAG_TRACE) or, with
+ * DLO_FLAG_TRACE_KERNELS alone, of every forward since the previous call that
+ * returned intervals (those are then cleared); cap entries at most, *n
+ * receives the number recorded (call with out = NULL to size the buffer; that
+ * clears nothing).  Times are in ms from the earliest recorded event.
+ * Synchronises the context's streams. */
 DLO_API dlo_status dlo_get_trace(dlo_ctx* ctx, dlo_interval* out, int32_t cap, int32_t* n);
 
 /* Message of the last failed call on this thread ("" if none). */

@@ -262,7 +262,15 @@ void build_chunks(Block& b, int dp, int64_t chunk) {
 }
 
 hipEvent_t next_ev(dlo_ctx* ctx) {
-  if (ctx->ev_next >= ctx->ev_pool.size()) return nullptr;
+  if (ctx->ev_next >= ctx->ev_pool.size()) {
+    // kernel-only tracing accumulates over forwards: grow the pool on demand
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;  // the interval is skipped
+    }
+    ctx->ev_pool.push_back(e);
+  }
   return ctx->ev_pool[ctx->ev_next++];
 }
 
@@ -594,7 +602,8 @@ extern "C" DLO_API dlo_status dlo_forward(dlo_ctx* ctx, float* x, const float* c
 
   const bool trace_all = (ctx->flags & DLO_FLAG_TRACE) != 0;
   const bool trace = trace_all || (ctx->flags & DLO_FLAG_TRACE_KERNELS) != 0;
-  if (trace) {
+  if (trace_all) {
+    // the full trace describes the last forward only
     ctx->trace.clear();
     ctx->ev_next = 0;
     ctx->trace_valid = false;
@@ -827,6 +836,12 @@ extern "C" DLO_API dlo_status dlo_get_trace(dlo_ctx* ctx, dlo_interval* out, int
   if (out) {
     if (cap < *n) return fail(DLO_E_INVAL, "cap %d < %d intervals", cap, *n);
     memcpy(out, tmp.data(), sizeof(dlo_interval) * tmp.size());
+    if (!(ctx->flags & DLO_FLAG_TRACE)) {
+      // kernel-only tracing: intervals handed out are consumed
+      ctx->trace.clear();
+      ctx->ev_next = 0;
+      ctx->trace_valid = false;
+    }
   }
   return DLO_OK;
 }

@@ -367,3 +367,21 @@ def test_kernel_trace_covers_every_step():
             for r in rs:
                 c = comp[r["block"]]
                 assert c["start"] <= r["start"] <= r["end"] <= c["end"]
+
+
+def test_kernel_trace_accumulates_until_read():
+    wl = synth.workload("tiny")
+    W = _weights(wl)
+    ctx = _ctx(list(wl.blocks), 4, wl.tokens, flags=dlo.FLAG_TRACE_KERNELS)
+    for b, flat in W.items():
+        ctx.load_shards(b, flat)
+    x, cond = synth.activations(wl.tokens, 256), synth.conditioning(256)
+    per_forward = wl.num_blocks * 10  # block compute + 9 kernels
+    for n in (1, 3):
+        for _ in range(n):
+            _run(ctx, x, cond)
+        tr = ctx.trace()  # hands out and clears
+        assert len(tr) == n * per_forward
+        assert sum(r["kind"] == "k_fc2" for r in tr) == n * wl.num_blocks
+        assert all(r["end"] >= r["start"] >= 0.0 for r in tr)
+    assert ctx.trace() == []
