@@ -103,10 +103,9 @@ def traffic_from_profiles(kernel_src, kind):
 
 
 def cpu_baseline(wl, dp, T, seconds):
-    """The oracle (numpy fp32, all weights resident) timed on the host cores
-    on a bounded sample of blocks of the same workload at the full token
-    count; blocks/s = blocks run / elapsed."""
-    import numpy as np
+    """The oracle as it stands (numpy, fp64, its default precision) timed on
+    the host cores on a bounded sample of blocks of the same workload at the
+    full token count; blocks/s = blocks run / elapsed."""
     import synth
     from oracle import dit as D, layout as OL
     try:
@@ -124,14 +123,14 @@ def cpu_baseline(wl, dp, T, seconds):
         if x.shape[1] != shp.d_model:
             x = D.width_adapter(x, shp.d_model)
         ts = time.perf_counter()
-        x = D.dit_block(flat, shp, x, cond, dtype=np.float32)
+        x = D.dit_block(flat, shp, x, cond)
         elapsed += time.perf_counter() - ts
         n += 1
         if elapsed >= seconds:
             break
     bps = n / elapsed
     return {"value": bps, "unit": "blocks/s", "cores": threads or os.cpu_count(), "kind": "oracle",
-            "sample": f"{n} of {wl.num_blocks} blocks of the {wl.name} workload at T={T}, numpy fp32, "
+            "sample": f"{n} of {wl.num_blocks} blocks of the {wl.name} workload at T={T}, numpy fp64, "
                       f"{elapsed:.1f} s of block compute (weight generation not timed)",
             "tokens_per_s": bps * T / wl.num_blocks}
 
