@@ -1,6 +1,6 @@
 // Kernel-level entry points: validate on the host, then launch the same
 // kernel dlo_forward launches for that step.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include "common.h"
 #include "dlo_ops.h"
