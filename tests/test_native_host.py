@@ -1,12 +1,20 @@
-"""Host-only C++ of the C ABI under AddressSanitizer + UndefinedBehaviorSanitizer.
+"""Host-only C++ of the library under AddressSanitizer + UndefinedBehaviorSanitizer.
 
-Builds ``tests/native/host_abi_check.cpp`` together with the library's
-host-only translation units (``layout.cpp``: block layout, ceil-division shard
-size, error reporting; ``ops.cpp``: validation and argument marshalling of the
-kernel-level entry points) with g++ and runs it.  The kernel launchers are
-replaced by recorders in the driver, so nothing touches a device; every
-out-of-bounds access, use after free, signed overflow or misaligned access in
-those files fails the run.  CPU only.
+Two drivers under ``tests/native/`` are built with g++ together with the
+library's host translation units and run; every out-of-bounds access, use
+after free, leak (where the HIP runtime is not linked), signed overflow or
+misaligned access in those files fails the run.  CPU only, nothing touches a
+device:
+
+* ``host_abi_check.cpp`` with ``layout.cpp`` (block layout, ceil-division
+  shard size, error reporting) and ``ops.cpp`` (validation and argument
+  marshalling of the kernel-level entry points); the kernel launchers are
+  recorders.
+* ``runtime_host_check.cpp`` with ``layout.cpp`` and ``runtime.cpp`` (context,
+  pinned shards, chunked staging, two-slot schedule, tracing, fail-closed
+  errors) against an in-order fake of the HIP runtime in which device memory
+  is host memory; the reconstruction launcher copies, the compute launchers
+  check that the slot they read holds the block's bf16 weights bit-exactly.
 """
 import os
 import shutil
@@ -64,3 +72,22 @@ def test_sanitizer_flags_catch_a_planted_overflow(tmp_path):
                        env=dict(os.environ, ASAN_OPTIONS="detect_leaks=0"))
     assert r.returncode != 0
     assert "heap-buffer-overflow" in r.stderr
+
+
+@pytest.mark.skipif(_toolchain_missing() is not None, reason=str(_toolchain_missing()))
+def test_runtime_host_logic_under_sanitizers(tmp_path):
+    """Shards, chunking, slot alternation across forwards, re-pointing,
+    validation and fail-closed errors of runtime.cpp, with a fake HIP runtime."""
+    exe = tmp_path / "runtime_host_check"
+    cmd = ["g++", "-std=c++17", "-g", "-O1", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include", f"-I{ROOT}/include", f"-I{CSRC}",
+           os.path.join(CSRC, "layout.cpp"), os.path.join(CSRC, "runtime.cpp"),
+           os.path.join(ROOT, "tests", "native", "runtime_host_check.cpp"), "-lpthread", "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-4000:]
+    # no HIP runtime is linked: leak checking stays on
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 0, (r.stdout + r.stderr)[-4000:]
+    assert "runtime host checks passed" in r.stdout
