@@ -103,9 +103,12 @@ def traffic_from_profiles(kernel_src, kind):
 
 
 def cpu_baseline(wl, dp, T, seconds):
-    """The oracle as it stands (numpy, fp64, its default precision) timed on
-    the host cores on a bounded sample of blocks of the same workload at the
-    full token count; blocks/s = blocks run / elapsed."""
+    """The oracle timed on the host cores on a bounded sample of blocks of the
+    same workload at the full token count; blocks/s = blocks run / elapsed.
+    `value` runs the oracle's arithmetic in fp32 (numpy with every BLAS
+    thread); the same oracle at its default fp64 is timed on a smaller
+    sample and reported beside it."""
+    import numpy as np
     import synth
     from oracle import dit as D, layout as OL
     try:
@@ -113,26 +116,33 @@ def cpu_baseline(wl, dp, T, seconds):
         threads = max([i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"] or [0])
     except Exception:
         threads = 0
-    x = synth.activations(T, wl.blocks[0].d_model)
-    cond = synth.conditioning(wl.blocks[0].d_cond)
-    n, t0 = 0, time.perf_counter()
-    elapsed = 0.0
-    for b in range(wl.num_blocks):
-        shp = wl.blocks[b]
-        flat = synth.block_weights(wl.wid, b, OL.block_numel(shp))
-        if x.shape[1] != shp.d_model:
-            x = D.width_adapter(x, shp.d_model)
-        ts = time.perf_counter()
-        x = D.dit_block(flat, shp, x, cond)
-        elapsed += time.perf_counter() - ts
-        n += 1
-        if elapsed >= seconds:
-            break
+
+    def timed(dtype, budget):
+        x = synth.activations(T, wl.blocks[0].d_model)
+        cond = synth.conditioning(wl.blocks[0].d_cond)
+        n, elapsed = 0, 0.0
+        for b in range(wl.num_blocks):
+            shp = wl.blocks[b]
+            flat = synth.block_weights(wl.wid, b, OL.block_numel(shp))
+            if x.shape[1] != shp.d_model:
+                x = D.width_adapter(x, shp.d_model)
+            ts = time.perf_counter()
+            x = D.dit_block(flat, shp, x, cond, dtype=dtype)
+            elapsed += time.perf_counter() - ts
+            n += 1
+            if elapsed >= budget:
+                break
+        return n, elapsed
+
+    n, elapsed = timed(np.float32, seconds)
+    n64, el64 = timed(np.float64, seconds / 2)
     bps = n / elapsed
     return {"value": bps, "unit": "blocks/s", "cores": threads or os.cpu_count(), "kind": "oracle",
-            "sample": f"{n} of {wl.num_blocks} blocks of the {wl.name} workload at T={T}, numpy fp64, "
+            "sample": f"{n} of {wl.num_blocks} blocks of the {wl.name} workload at T={T}, numpy fp32, "
                       f"{elapsed:.1f} s of block compute (weight generation not timed)",
-            "tokens_per_s": bps * T / wl.num_blocks}
+            "tokens_per_s": bps * T / wl.num_blocks,
+            "fp64": {"value": n64 / el64, "unit": "blocks/s",
+                     "sample": f"{n64} of {wl.num_blocks} blocks, numpy fp64 (the oracle's default), {el64:.1f} s"}}
 
 
 def main():
