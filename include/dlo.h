@@ -95,7 +95,9 @@ typedef int32_t dlo_status;
                                        events off the copy and gather streams.
                                        Without DLO_FLAG_TRACE the intervals
                                        accumulate over forwards until
-                                       dlo_get_trace hands them out */
+                                       dlo_get_trace hands them out (at most
+                                       2^19 per context; later ones are not
+                                       recorded until then) */
 
 typedef struct dlo_ctx dlo_ctx;
 

@@ -58,6 +58,7 @@ constexpr size_t kAlign = 256;
 constexpr int64_t kDefaultChunk = int64_t(1) << 26;
 constexpr int64_t kMinChunk = 4096;
 constexpr int kLandSlack = 8;  // landing offset (elements) used to co-align with the slot
+constexpr size_t kMaxTraceEvents = size_t(1) << 20;  // bound on recorded trace events per context
 
 // One H2D transfer.  The dp shards of a block sit back to back in one pinned
 // region (shard r at element r * S), so their concatenation -- the gather's
@@ -263,7 +264,9 @@ void build_chunks(Block& b, int dp, int64_t chunk) {
 
 hipEvent_t next_ev(dlo_ctx* ctx) {
   if (ctx->ev_next >= ctx->ev_pool.size()) {
-    // kernel-only tracing accumulates over forwards: grow the pool on demand
+    // kernel-only tracing accumulates over forwards: grow the pool on demand,
+    // up to a bound (intervals past it are skipped until the trace is read)
+    if (ctx->ev_pool.size() >= kMaxTraceEvents) return nullptr;
     hipEvent_t e = nullptr;
     if (hipEventCreate(&e) != hipSuccess) {
       (void)hipGetLastError();
