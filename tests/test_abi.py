@@ -148,3 +148,15 @@ def test_op_validation_without_launch():
     assert lib.dlo_op_ln_modulate(fake, 64, None, fake, fake, fake, 4, 8194, None) == L.E_SHAPE
     assert lib.dlo_op_assemble(fake, fake + 2, 8, None) == L.E_INVAL  # overlap
     assert lib.dlo_op_assemble(fake, fake, 0, None) == L.OK           # empty copy is a no-op
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asking for more exits with a message before
+    touching any device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
