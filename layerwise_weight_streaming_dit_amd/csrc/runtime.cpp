@@ -59,6 +59,11 @@ constexpr int64_t kDefaultChunk = int64_t(1) << 26;
 constexpr int64_t kMinChunk = 4096;
 constexpr int kLandSlack = 8;  // landing offset (elements) used to co-align with the slot
 constexpr size_t kMaxTraceEvents = size_t(1) << 20;  // bound on recorded trace events per context
+// Trace events only time intervals (the host reads them after synchronizing
+// the streams; no stream waits on them), so they skip the system-scope
+// release a default event performs when recorded: that cache write-back sat
+// between every pair of traced kernels and lengthened each traced interval.
+constexpr unsigned kTraceEventFlags = hipEventDisableSystemFence;
 
 // One H2D transfer.  The dp shards of a block sit back to back in one pinned
 // region (shard r at element r * S), so their concatenation -- the gather's
@@ -268,7 +273,7 @@ hipEvent_t next_ev(dlo_ctx* ctx) {
     // up to a bound (intervals past it are skipped until the trace is read)
     if (ctx->ev_pool.size() >= kMaxTraceEvents) return nullptr;
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) {
+    if (hipEventCreateWithFlags(&e, kTraceEventFlags) != hipSuccess) {
       (void)hipGetLastError();
       return nullptr;  // the interval is skipped
     }
@@ -545,7 +550,7 @@ extern "C" DLO_API dlo_status dlo_create(const dlo_config* cfg, dlo_ctx** out) {
     size_t n = 0;
     for (auto& b : c->blocks) n += 4 * b.chunks.size() + 2 + 2 * 9;
     c->ev_pool.resize(n, nullptr);
-    for (size_t i = 0; i < n; ++i) DLO_HIP(nullptr, hipEventCreate(&c->ev_pool[i]));
+    for (size_t i = 0; i < n; ++i) DLO_HIP(nullptr, hipEventCreateWithFlags(&c->ev_pool[i], kTraceEventFlags));
   }
   DLO_HIP(nullptr, hipStreamSynchronize(c->gather_s));
   *out = ctx.release();
