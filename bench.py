@@ -86,11 +86,14 @@ def source_hash(path):
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_src, kind):
+def traffic_from_profiles(kernel_src, kind, workload):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter
     summary (profiles/hbm_traffic_image_dit.txt: lines "kind source-sha16
-    fetch-bytes write-bytes", copy-calibrated), used only if the summary was
-    taken on the current kernel source and device headers; else None."""
+    fetch-bytes write-bytes", copy-calibrated), used only for the workload the
+    counters were taken on (image) and only if they were taken on the current
+    kernel source and device headers; else None."""
+    if workload != "image":
+        return None
     p = os.path.join(ROOT, "profiles", "hbm_traffic_image_dit.txt")
     if not os.path.exists(p):
         return None
@@ -335,7 +338,7 @@ def main():
                 "peak": PEAK_BF16_TFLOPS if unit == "flop" else PEAK_HBM_GBPS,
                 "unit": "TFLOP/s" if unit == "flop" else "GB/s",
                 "frac": ach / (PEAK_BF16_TFLOPS if unit == "flop" else PEAK_HBM_GBPS),
-                "traffic": traffic_from_profiles(src, dom),
+                "traffic": traffic_from_profiles(src, dom, wl.name),
                 "kernel": f"{dom}: {KERNEL_DESC[dom]}", "avg_launch_ms": kernels[dom]["avg_ms"],
                 "work_per_launch": work, "work_unit": unit}
 
