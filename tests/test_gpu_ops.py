@@ -175,29 +175,39 @@ def test_gemm_large_tile_shapes():
         assert ok, (M, N, K, ma, mr)
 
 
-@pytest.mark.parametrize("epi", [dlo.EPI_BIAS_F16, dlo.EPI_GATED_F32])
-@pytest.mark.parametrize("M,N,K", [(4000, 2048, 4096), (4096 + 17, 4096, 1024)])
+@pytest.mark.parametrize("epi,M,N,K", [(dlo.EPI_BIAS_F16, 4000, 2048, 4096), (dlo.EPI_GATED_F32, 4000, 2048, 4096),
+                                         (dlo.EPI_VT_F16, 4000, 2048, 4096), (dlo.EPI_BIAS_F16, 4096 + 17, 4096, 1024),
+                                         (dlo.EPI_GATED_F32, 4096 + 17, 4096, 1024)])
 def test_gemm_long_k_and_ragged_large_tiles(epi, M, N, K):
-    """The 256x128 tile (K >= 4096, the MLP-down shape class) and the
-    256x256 tile with a ragged last tile row, checked on sampled rows (every
-    row of the last, partial tile row included) against fp64 products."""
+    """The 256x128 tile (K >= 4096, the MLP-down shape class, and the
+    transposed v projection of a d = 4096 block at T <= 2048) and the 256x256
+    tile with a ragged last tile row, checked on sampled rows (every row of
+    the last, partial tile row included) against fp64 products."""
     rng = np.random.default_rng(M + N + K + epi)
-    a = _f16(rng.standard_normal((M, K)))
-    w = _bf16(rng.standard_normal((N, K)) * 0.02)
-    bias = _bf16(rng.standard_normal(N) * 0.1)
+    vt = epi == dlo.EPI_VT_F16
+    w_rows = N - 77 if vt else N  # transposed v: columns past the last token repeat it
+    a = _bf16(rng.standard_normal((M, K)) * 0.02) if vt else _f16(rng.standard_normal((M, K)))
+    w = _f16(rng.standard_normal((w_rows, K))) if vt else _bf16(rng.standard_normal((N, K)) * 0.02)
+    bias = _bf16(rng.standard_normal(M if vt else N) * 0.1)
     gate = rng.standard_normal(N).astype(np.float32)
     x0 = rng.standard_normal((M, N)).astype(np.float32)
     t = torch()
     out = dev(x0.copy()) if epi == dlo.EPI_GATED_F32 else t.empty((M, N), dtype=t.int16, device="cuda")
-    dlo.op_gemm(epi, dev(a), K, dev(w), K, N, dev(bias), dev(gate), out, N, M, N, K)
+    dlo.op_gemm(epi, dev(a), K, dev(w), K, w_rows, dev(bias), dev(gate), out, N, M, N, K)
     rows = np.unique(np.concatenate([rng.choice(M, 48, replace=False), np.arange(M // 256 * 256, M)]))
-    acc = f16_to_f64(a[rows]) @ bf16_to_f64(w).reshape(N, K).T + bf16_to_f64(bias)
-    if epi == dlo.EPI_GATED_F32:
-        got = host(out).astype(np.float64)[rows]
-        want = x0[rows].astype(np.float64) + gate.astype(np.float64) * acc
-    else:
-        got = f16_to_f64(host(out, np.uint16))[rows]
+    if vt:
+        wf = f16_to_f64(w).reshape(w_rows, K)[np.minimum(np.arange(N), w_rows - 1)]
+        acc = bf16_to_f64(a[rows]).reshape(len(rows), K) @ wf.T + bf16_to_f64(bias)[rows][:, None]
+        got = f16_to_f64(host(out, np.uint16))[rows][:, vt_position(np.arange(N))]
         want = acc
+    else:
+        acc = f16_to_f64(a[rows]) @ bf16_to_f64(w).reshape(N, K).T + bf16_to_f64(bias)
+        if epi == dlo.EPI_GATED_F32:
+            got = host(out).astype(np.float64)[rows]
+            want = x0[rows].astype(np.float64) + gate.astype(np.float64) * acc
+        else:
+            got = f16_to_f64(host(out, np.uint16))[rows]
+            want = acc
     ok, ma, mr = within(got, want, rtol=2e-3, atol=2e-3)
     assert ok, (M, N, K, ma, mr)
 
