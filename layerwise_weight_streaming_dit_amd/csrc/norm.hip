@@ -12,7 +12,10 @@ constexpr int kNormThreads = 256;
 constexpr int kAdaRowsPerWave = 4;
 
 // mod[r] = W[r] . silu(cond) + b[r].  silu(cond) is staged once per workgroup
-// in LDS; each wave walks kAdaRowsPerWave rows with 8-byte bf16 loads.
+// in LDS; each wave computes kAdaRowsPerWave rows at once: the rows' loads
+// (8 bytes per lane per 256 columns) and their biases are all issued before
+// any arithmetic, and the rows' wave reductions are independent chains, so
+// the GEMV costs a few memory round trips per wave instead of a few per row.
 __global__ __launch_bounds__(kNormThreads) void adaln_kernel(const uint16_t* __restrict__ w,
                                                              const uint16_t* __restrict__ b,
                                                              const float* __restrict__ cond,
@@ -23,20 +26,29 @@ __global__ __launch_bounds__(kNormThreads) void adaln_kernel(const uint16_t* __r
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r0 = (blockIdx.x * (kNormThreads / 64) + wave) * kAdaRowsPerWave;
+  // rows past the end read the last row (in bounds) and store nothing
+  const float bias = bf16_to_f32(b[min(r0 + min(lane, kAdaRowsPerWave - 1), rows - 1)]);
+  float acc[kAdaRowsPerWave];
+#pragma unroll
+  for (int rr = 0; rr < kAdaRowsPerWave; ++rr) acc[rr] = 0.f;
+  for (int j = lane * 4; j < c; j += 256) {
+    u32x2_t v[kAdaRowsPerWave];
+#pragma unroll
+    for (int rr = 0; rr < kAdaRowsPerWave; ++rr)
+      v[rr] = *reinterpret_cast<const u32x2_t*>(w + static_cast<int64_t>(min(r0 + rr, rows - 1)) * c + j);
+    const f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(sc + j);
+#pragma unroll
+    for (int rr = 0; rr < kAdaRowsPerWave; ++rr)
+      acc[rr] += __uint_as_float(v[rr].x << 16) * s4.x + __uint_as_float(v[rr].x & 0xffff0000u) * s4.y +
+                 __uint_as_float(v[rr].y << 16) * s4.z + __uint_as_float(v[rr].y & 0xffff0000u) * s4.w;
+  }
+  float mine = 0.f;
 #pragma unroll
   for (int rr = 0; rr < kAdaRowsPerWave; ++rr) {
-    const int r = r0 + rr;
-    if (r >= rows) break;
-    const uint16_t* wr = w + static_cast<int64_t>(r) * c;
-    float acc = 0.f;
-    for (int j = lane * 4; j < c; j += 256) {
-      const u32x2_t v = *reinterpret_cast<const u32x2_t*>(wr + j);
-      acc += __uint_as_float(v.x << 16) * sc[j] + __uint_as_float(v.x & 0xffff0000u) * sc[j + 1] +
-             __uint_as_float(v.y << 16) * sc[j + 2] + __uint_as_float(v.y & 0xffff0000u) * sc[j + 3];
-    }
-    acc = wave_sum(acc);
-    if (lane == 0) mod[r] = acc + bf16_to_f32(b[r]);
+    const float t = wave_sum(acc[rr]);
+    if (lane == rr) mine = t;
   }
+  if (lane < kAdaRowsPerWave && r0 + lane < rows) mod[r0 + lane] = mine + bias;
 }
 
 // One wave per token row, four rows per workgroup: the row (adapted to width
