@@ -315,9 +315,12 @@ def main():
         if not rs:
             continue
         avg = dur(rs) / len(rs)
+        ds = sorted(r["end"] - r["start"] for r in rs)
         unit, work = kernel_work(shapes[0], T)[kind]
         rate = work / (avg * 1e-3)
-        e = {"launches": len(rs), "avg_ms": avg, "total_ms": dur(rs), "desc": KERNEL_DESC[kind]}
+        # the median shows how far a few slow launches pull the average
+        e = {"launches": len(rs), "avg_ms": avg, "median_ms": ds[len(ds) // 2], "total_ms": dur(rs),
+             "desc": KERNEL_DESC[kind]}
         if unit == "flop":
             e["TFLOPs"] = rate / 1e12
             e["mfma_frac"] = rate / 1e12 / PEAK_BF16_TFLOPS
