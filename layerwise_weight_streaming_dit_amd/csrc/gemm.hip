@@ -356,10 +356,119 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
       }
     }
   };
-  if (m0 + BM <= g.M && n0 + BN <= g.N)
-    rows_out(std::false_type{});
-  else
-    rows_out(std::true_type{});
+  // fp16 outputs go out through LDS: the C^T accumulator layout gives each
+  // lane 8 bytes of 32 different rows per store (16-byte pieces of 32 rows
+  // per instruction); staged row-major in the idle stage buffers, each
+  // instruction instead writes 8 rows x 128 contiguous bytes (the wave's 64
+  // columns).  Two tile rows (64 output rows) per pass.
+  auto rows_out_lds = [&](auto guarded) {
+    constexpr bool GUARD = decltype(guarded)::value;
+    constexpr int RS = 72;  // LDS row stride in halves (16-byte aligned rows)
+    constexpr int PR = 64;  // output rows per pass
+    static_assert(WTN == 64 && WTM % PR == 0, "wave tile");
+    static_assert((W / 4) * PR * RS * 2 <= STAGE_B * 2 && STAGE_B <= STAGE_A && W % 4 == 0, "epilogue region");
+    __syncthreads();  // every wave is done reading the stage buffers
+    const int arr = wave / (W / 4), sub = wave % (W / 4);
+    uint16_t* region = (arr == 0 ? sA0 : arr == 1 ? sA1 : arr == 2 ? sB0 : sB1) + sub * PR * RS;
+#pragma unroll
+    for (int p = 0; p < WTM / PR; ++p) {
+#pragma unroll
+      for (int i = 0; i < PR / 32; ++i) {
+        const int tm = p * (PR / 32) + i;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(g.bias + min(col[tn][q], g.N - 4));
+            f32x4_t v;
+            v.x = acc[tm][tn][4 * q] + __uint_as_float(bb.x << 16);
+            v.y = acc[tm][tn][4 * q + 1] + __uint_as_float(bb.x & 0xffff0000u);
+            v.z = acc[tm][tn][4 * q + 2] + __uint_as_float(bb.y << 16);
+            v.w = acc[tm][tn][4 * q + 3] + __uint_as_float(bb.y & 0xffff0000u);
+            if constexpr (EPI == EPI_BIAS_GELU_F16) {
+              v.x = gelu_tanh(v.x);
+              v.y = gelu_tanh(v.y);
+              v.z = gelu_tanh(v.z);
+              v.w = gelu_tanh(v.w);
+            }
+            u32x2_t w;
+            w.x = pack_f16x2(v.x, v.y);
+            w.y = pack_f16x2(v.z, v.w);
+            *reinterpret_cast<u32x2_t*>(region + (i * 32 + (lane & 31)) * RS + tn * 32 + 8 * q + 4 * (lane >> 5)) = w;
+          }
+      }
+#pragma unroll
+      for (int k = 0; k < PR / 8; ++k) {
+        const int r = k * 8 + (lane >> 3), c8 = (lane & 7) * 8;
+        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(region + r * RS + c8);
+        const int row = m0 + wm * WTM + p * PR + r, cc = n0 + wn * WTN + c8;
+        if (!GUARD || (row < g.M && cc < g.N))
+          *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(g.out) + static_cast<int64_t>(row) * g.ldo + cc) = val;
+      }
+    }
+  };
+  // The gated fp32 residual likewise: acc + bias is staged row-major (one
+  // tile row, 32 output rows, per pass), then each instruction reads and
+  // writes 4 rows x 256 contiguous bytes of x, x = fma(gate, acc + bias, x)
+  // exactly as before.
+  auto rows_out_lds_f32 = [&](auto guarded) {
+    constexpr bool GUARD = decltype(guarded)::value;
+    constexpr int RS = 68;  // LDS row stride in floats (16-byte aligned rows)
+    static_assert(WTN == 64, "wave tile");
+    static_assert((W / 4) * 32 * RS * 4 <= STAGE_B * 2 && STAGE_B <= STAGE_A && W % 4 == 0, "epilogue region");
+    __syncthreads();  // every wave is done reading the stage buffers
+    const int arr = wave / (W / 4), sub = wave % (W / 4);
+    float* region = reinterpret_cast<float*>(arr == 0 ? sA0 : arr == 1 ? sA1 : arr == 2 ? sB0 : sB1) + sub * 32 * RS;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(g.bias + min(col[tn][q], g.N - 4));
+          f32x4_t v;
+          v.x = acc[tm][tn][4 * q] + __uint_as_float(bb.x << 16);
+          v.y = acc[tm][tn][4 * q + 1] + __uint_as_float(bb.x & 0xffff0000u);
+          v.z = acc[tm][tn][4 * q + 2] + __uint_as_float(bb.y << 16);
+          v.w = acc[tm][tn][4 * q + 3] + __uint_as_float(bb.y & 0xffff0000u);
+          *reinterpret_cast<f32x4_t*>(region + (lane & 31) * RS + tn * 32 + 8 * q + 4 * (lane >> 5)) = v;
+        }
+      const int c4 = (lane & 15) * 4, cc = n0 + wn * WTN + c4;
+      const f32x4_t gt = *reinterpret_cast<const f32x4_t*>(g.gate + (GUARD ? min(cc, g.N - 4) : cc));
+      f32x4_t xr[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int row = m0 + wm * WTM + tm * 32 + k * 4 + (lane >> 4);
+        const int64_t off = static_cast<int64_t>(GUARD ? min(row, g.M - 1) : row) * g.ldo + (GUARD ? min(cc, g.N - 4) : cc);
+        xr[k] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(g.out) + off);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = k * 4 + (lane >> 4);
+        const int row = m0 + wm * WTM + tm * 32 + r;
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(region + r * RS + c4);
+        if (!GUARD || (row < g.M && cc < g.N))
+          *reinterpret_cast<f32x4_t*>(static_cast<float*>(g.out) + static_cast<int64_t>(row) * g.ldo + cc) = xr[k] + gt * v;
+      }
+    }
+  };
+  const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;
+  if constexpr (EPI == EPI_BIAS_F16 || EPI == EPI_BIAS_GELU_F16) {
+    if (interior)
+      rows_out_lds(std::false_type{});
+    else
+      rows_out_lds(std::true_type{});
+  } else if constexpr (EPI == EPI_GATED_F32) {
+    if (interior)
+      rows_out_lds_f32(std::false_type{});
+    else
+      rows_out_lds_f32(std::true_type{});
+  } else {
+    if (interior)
+      rows_out(std::false_type{});
+    else
+      rows_out(std::true_type{});
+  }
 }
 
 template <int BM, int BN, int WM, int WN, int PFD>
