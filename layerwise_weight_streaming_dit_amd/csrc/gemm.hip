@@ -268,99 +268,24 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
   // ---- epilogue.  The MFMAs above take W as their first operand, so each
   // 32x32 accumulator is a tile of C^T: lane l owns output row (l % 32) of the
   // tile and, for q = 0..3, the four consecutive output columns
-  // 8q + 4(l / 32) + 0..3 (registers 4q..4q+3) -- one 8-byte bf16 store or
-  // one 16-byte fp32 load/store each.  N is a multiple of 16, so a group of
-  // four columns is either wholly inside or wholly past the last column.
-  //
-  // Every load comes before the stores it feeds: the epilogue walks the
-  // tile in batches (one tile row and CB tile columns), loads everything a
-  // batch reads -- fp32 residual, gate, bias -- then computes and stores it.
-  // A load placed after a store to the output cannot move above it (the
-  // compiler cannot rule out that they alias), so without batching every
-  // 16-byte group was its own round trip to memory.  The 256x128 tile (one
-  // wave per SIMD, registers to spare) takes a whole tile row per batch, the
-  // others one tile column.  A tile wholly inside the output (the usual
-  // case) stores without per-lane guards, so no branch splits a batch; an
-  // edge tile loads from clamped addresses and guards every store.
-  constexpr int CB = (BM == 256 && BN == 128) ? TN : 1;
+  // 8q + 4(l / 32) + 0..3 (registers 4q..4q+3).  N is a multiple of 16, so a
+  // group of four (or eight) columns is either wholly inside or wholly past
+  // the last column.
   int col[TN][4];
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
     for (int q = 0; q < 4; ++q) col[tn][q] = n0 + wn * WTN + tn * 32 + 8 * q + 4 * (lane >> 5);
-  auto rows_out = [&](auto guarded) {
-    constexpr bool GUARD = decltype(guarded)::value;
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      const int row = m0 + wm * WTM + tm * 32 + (lane & 31);
-      const bool row_ok = !GUARD || row < g.M;
-      const int rr = GUARD ? min(row, g.M - 1) : row;
-      const int64_t orow = static_cast<int64_t>(rr) * g.ldo;
-      float rbias = 0.f;
-      if constexpr (EPI == EPI_VT_F16) rbias = bf16_to_f32(g.bias[rr]);
-#pragma unroll
-      for (int t0 = 0; t0 < TN; t0 += CB) {
-        u32x2_t braw[CB][4];
-        f32x4_t gt[CB][4], xr[CB][4];
-#pragma unroll
-        for (int j = 0; j < CB; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int cc = GUARD ? min(col[t0 + j][q], g.N - 4) : col[t0 + j][q];
-            if constexpr (EPI != EPI_VT_F16) braw[j][q] = *reinterpret_cast<const u32x2_t*>(g.bias + cc);
-            if constexpr (EPI == EPI_GATED_F32) {
-              gt[j][q] = *reinterpret_cast<const f32x4_t*>(g.gate + cc);
-              xr[j][q] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(g.out) + orow + cc);
-            }
-          }
-#pragma unroll
-        for (int j = 0; j < CB; ++j) {
-          const int tn = t0 + j;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (GUARD && (!row_ok || col[tn][q] >= g.N)) continue;
-            f32x4_t v;
-            v.x = acc[tm][tn][4 * q];
-            v.y = acc[tm][tn][4 * q + 1];
-            v.z = acc[tm][tn][4 * q + 2];
-            v.w = acc[tm][tn][4 * q + 3];
-            if constexpr (EPI == EPI_VT_F16) {
-              // transposed v: tokens col..col+3 land at their permuted key
-              // positions, which are consecutive (only bits 2 and 3 move)
-              v += rbias;
-              u32x2_t w;
-              w.x = pack_f16x2(v.x, v.y);
-              w.y = pack_f16x2(v.z, v.w);
-              *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(g.out) + orow + vt_key_position(col[tn][q])) = w;
-            } else {
-              const u32x2_t bb = braw[j][q];
-              v += f32x4_t{__uint_as_float(bb.x << 16), __uint_as_float(bb.x & 0xffff0000u),
-                           __uint_as_float(bb.y << 16), __uint_as_float(bb.y & 0xffff0000u)};
-              if constexpr (EPI == EPI_GATED_F32) {
-                *reinterpret_cast<f32x4_t*>(static_cast<float*>(g.out) + orow + col[tn][q]) = xr[j][q] + gt[j][q] * v;
-              } else {
-                if constexpr (EPI == EPI_BIAS_GELU_F16) {
-                  v.x = gelu_tanh(v.x);
-                  v.y = gelu_tanh(v.y);
-                  v.z = gelu_tanh(v.z);
-                  v.w = gelu_tanh(v.w);
-                }
-                u32x2_t w;
-                w.x = pack_f16x2(v.x, v.y);
-                w.y = pack_f16x2(v.z, v.w);
-                *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(g.out) + orow + col[tn][q]) = w;
-              }
-            }
-          }
-        }
-      }
-    }
-  };
-  // fp16 outputs go out through LDS: the C^T accumulator layout gives each
-  // lane 8 bytes of 32 different rows per store (16-byte pieces of 32 rows
-  // per instruction); staged row-major in the idle stage buffers, each
-  // instruction instead writes 8 rows x 128 contiguous bytes (the wave's 64
-  // columns).  Two tile rows (64 output rows) per pass.
+  // Outputs go out through LDS.  In the C^T accumulator layout a lane holds
+  // 4 consecutive columns of 32 different rows, so a direct store writes
+  // 8- or 16-byte pieces of 32 rows per instruction (and the gated residual's
+  // loads, placed after stores to the same buffer, could not be batched).
+  // Staged row-major in the idle stage buffers (padded rows, one region per
+  // wave), each instruction instead moves whole row segments: fp16 outputs
+  // 8 rows x 128 bytes (the wave's 64 columns; two tile rows per pass), the
+  // fp32 residual 4 rows x 256 bytes (one tile row per pass).  Interior
+  // tiles store unguarded; edge tiles clamp their loads and guard their
+  // stores.
   auto rows_out_lds = [&](auto guarded) {
     constexpr bool GUARD = decltype(guarded)::value;
     constexpr int RS = 72;  // LDS row stride in halves (16-byte aligned rows)
@@ -379,12 +304,26 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
         for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(g.bias + min(col[tn][q], g.N - 4));
             f32x4_t v;
-            v.x = acc[tm][tn][4 * q] + __uint_as_float(bb.x << 16);
-            v.y = acc[tm][tn][4 * q + 1] + __uint_as_float(bb.x & 0xffff0000u);
-            v.z = acc[tm][tn][4 * q + 2] + __uint_as_float(bb.y << 16);
-            v.w = acc[tm][tn][4 * q + 3] + __uint_as_float(bb.y & 0xffff0000u);
+            v.x = acc[tm][tn][4 * q];
+            v.y = acc[tm][tn][4 * q + 1];
+            v.z = acc[tm][tn][4 * q + 2];
+            v.w = acc[tm][tn][4 * q + 3];
+            int c = tn * 32 + 8 * q + 4 * (lane >> 5);  // column in the wave's 64
+            if constexpr (EPI == EPI_VT_F16) {
+              // transposed v: per-row bias; tokens c..c+3 land at their
+              // permuted key positions, consecutive too (the tile's first
+              // column is a multiple of 16, and only bits 2 and 3 move)
+              const float rb = bf16_to_f32(g.bias[min(m0 + wm * WTM + tm * 32 + (lane & 31), g.M - 1)]);
+              v += rb;
+              c = vt_key_position(c);
+            } else {
+              const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(g.bias + min(col[tn][q], g.N - 4));
+              v.x += __uint_as_float(bb.x << 16);
+              v.y += __uint_as_float(bb.x & 0xffff0000u);
+              v.z += __uint_as_float(bb.y << 16);
+              v.w += __uint_as_float(bb.y & 0xffff0000u);
+            }
             if constexpr (EPI == EPI_BIAS_GELU_F16) {
               v.x = gelu_tanh(v.x);
               v.y = gelu_tanh(v.y);
@@ -394,7 +333,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
             u32x2_t w;
             w.x = pack_f16x2(v.x, v.y);
             w.y = pack_f16x2(v.z, v.w);
-            *reinterpret_cast<u32x2_t*>(region + (i * 32 + (lane & 31)) * RS + tn * 32 + 8 * q + 4 * (lane >> 5)) = w;
+            *reinterpret_cast<u32x2_t*>(region + (i * 32 + (lane & 31)) * RS + c) = w;
           }
       }
 #pragma unroll
@@ -407,10 +346,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
       }
     }
   };
-  // The gated fp32 residual likewise: acc + bias is staged row-major (one
-  // tile row, 32 output rows, per pass), then each instruction reads and
-  // writes 4 rows x 256 contiguous bytes of x, x = fma(gate, acc + bias, x)
-  // exactly as before.
+  // Gated fp32 residual: acc + bias is staged, then x = x + gate * (acc + bias)
+  // (one fused multiply-add) row segment by row segment, the tile row's x
+  // loads all issued before its stores.
   auto rows_out_lds_f32 = [&](auto guarded) {
     constexpr bool GUARD = decltype(guarded)::value;
     constexpr int RS = 68;  // LDS row stride in floats (16-byte aligned rows)
@@ -453,21 +391,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
     }
   };
   const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;
-  if constexpr (EPI == EPI_BIAS_F16 || EPI == EPI_BIAS_GELU_F16) {
+  if constexpr (EPI == EPI_BIAS_F16 || EPI == EPI_BIAS_GELU_F16 || EPI == EPI_VT_F16) {
     if (interior)
       rows_out_lds(std::false_type{});
     else
       rows_out_lds(std::true_type{});
-  } else if constexpr (EPI == EPI_GATED_F32) {
+  } else {
     if (interior)
       rows_out_lds_f32(std::false_type{});
     else
       rows_out_lds_f32(std::true_type{});
-  } else {
-    if (interior)
-      rows_out(std::false_type{});
-    else
-      rows_out(std::true_type{});
   }
 }
 
