@@ -176,13 +176,17 @@ def test_gemm_large_tile_shapes():
 
 
 @pytest.mark.parametrize("epi,M,N,K", [(dlo.EPI_BIAS_F16, 4000, 2048, 4096), (dlo.EPI_GATED_F32, 4000, 2048, 4096),
-                                         (dlo.EPI_VT_F16, 4000, 2048, 4096), (dlo.EPI_BIAS_F16, 4096 + 17, 4096, 1024),
-                                         (dlo.EPI_GATED_F32, 4096 + 17, 4096, 1024)])
+                                         (dlo.EPI_VT_F16, 4000, 2048, 4096), (dlo.EPI_BIAS_GELU_F16, 4000, 2048, 4096),
+                                         (dlo.EPI_BIAS_F16, 4096 + 17, 4096, 1024),
+                                         (dlo.EPI_GATED_F32, 4096 + 17, 4096, 1024),
+                                         (dlo.EPI_BIAS_GELU_F16, 4096 + 17, 4096 - 48, 1024),
+                                         (dlo.EPI_VT_F16, 4096 + 128, 4096 - 64, 1024)])
 def test_gemm_long_k_and_ragged_large_tiles(epi, M, N, K):
     """The 256x128 tile (K >= 4096, the MLP-down shape class, and the
     transposed v projection of a d = 4096 block at T <= 2048) and the 256x256
-    tile with a ragged last tile row, checked on sampled rows (every row of
-    the last, partial tile row included) against fp64 products."""
+    tile with a ragged last tile row and column, every epilogue, checked on
+    sampled rows (every row of the last, partial tile row included) against
+    fp64 products."""
     rng = np.random.default_rng(M + N + K + epi)
     vt = epi == dlo.EPI_VT_F16
     w_rows = N - 77 if vt else N  # transposed v: columns past the last token repeat it
@@ -205,6 +209,9 @@ def test_gemm_long_k_and_ragged_large_tiles(epi, M, N, K):
         if epi == dlo.EPI_GATED_F32:
             got = host(out).astype(np.float64)[rows]
             want = x0[rows].astype(np.float64) + gate.astype(np.float64) * acc
+        elif epi == dlo.EPI_BIAS_GELU_F16:
+            got = f16_to_f64(host(out, np.uint16))[rows]
+            want = D.gelu_tanh(acc)
         else:
             got = f16_to_f64(host(out, np.uint16))[rows]
             want = acc
