@@ -316,11 +316,14 @@ def main():
             continue
         avg = dur(rs) / len(rs)
         ds = sorted(r["end"] - r["start"] for r in rs)
-        unit, work = kernel_work(shapes[0], T)[kind]
+        # work per launch follows each launch's block (widths differ between
+        # blocks in the irregular workload); average work / average time
+        unit = kernel_work(shapes[0], T)[kind][0]
+        work = sum(kernel_work(shapes[r["block"]], T)[kind][1] for r in rs) / len(rs)
         rate = work / (avg * 1e-3)
         # the median shows how far a few slow launches pull the average
         e = {"launches": len(rs), "avg_ms": avg, "median_ms": ds[len(ds) // 2], "total_ms": dur(rs),
-             "desc": KERNEL_DESC[kind]}
+             "work_per_launch": work, "desc": KERNEL_DESC[kind]}
         if unit == "flop":
             e["TFLOPs"] = rate / 1e12
             e["mfma_frac"] = rate / 1e12 / PEAK_BF16_TFLOPS
@@ -329,11 +332,11 @@ def main():
             e["hbm_frac"] = rate / 1e9 / PEAK_HBM_GBPS
         kernels[kind] = e
     gemm_kinds = [k for k in ("k_qk", "k_v", "k_out", "k_fc1", "k_fc2") if k in kernels]
-    gemm_flops = sum(kernel_work(shapes[0], T)[k][1] * kernels[k]["launches"] for k in gemm_kinds)
+    gemm_flops = sum(kernels[k]["work_per_launch"] * kernels[k]["launches"] for k in gemm_kinds)
     gemm_ms = sum(kernels[k]["total_ms"] for k in gemm_kinds)
     gemm_util = gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS if gemm_ms else None
     dom = max(kernels, key=lambda k: kernels[k]["total_ms"])
-    unit, work = kernel_work(shapes[0], T)[dom]
+    unit, work = kernel_work(shapes[0], T)[dom][0], kernels[dom]["work_per_launch"]
     ach = kernels[dom]["TFLOPs"] if unit == "flop" else kernels[dom]["GBps"]
     src = os.path.join(ROOT, "layerwise_weight_streaming_dit_amd", "csrc",
                        "attention.hip" if dom == "k_attn" else ("gemm.hip" if unit == "flop" else "norm.hip"))
