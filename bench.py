@@ -424,7 +424,11 @@ def main():
         "overlap": {"E": overlap_E, "hidden_frac": hidden, "t_forward_ms": t_fwd, "sum_h2d_ms": h2d_ms,
                     "sum_asm_ms": asm_ms, "sum_compute_ms": comp_ms, "serialized_ms": serial,
                     "steady_state": steady},
-        "residency": {"high_water_blocks": st["residency_high_water"], "slot_bytes": st["slot_bytes"],
+        "residency": {"high_water_blocks": st["residency_high_water"],
+                      "high_water_note": "most blocks whose slot was occupied at one instant (from the block's first "
+                                         "reconstruction write to the end of its compute); 1 when the host link "
+                                         "is the bottleneck, since block b+1 lands only after block b computed",
+                      "slot_bytes": st["slot_bytes"],
                       "landing_bytes": st["landing_bytes"], "workspace_bytes": st["workspace_bytes"]},
         "kernels": kernels,
         "roofline": roofline,
