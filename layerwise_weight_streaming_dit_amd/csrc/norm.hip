@@ -56,13 +56,20 @@ __global__ __launch_bounds__(kNormThreads) void adaln_kernel(const uint16_t* __r
 // variance are wave reductions with no LDS or barrier, and every lane has NV
 // loads in flight.  The register cap keeps 4 waves per SIMD resident for
 // d <= 2048, 2 up to 4096; wider rows use the workgroup-per-row kernel below.
+//
+// shift and scale are shared by the workgroup's four rows: they are staged in
+// LDS once (their loads overlap the rows' loads), so the output loop reads
+// them from LDS -- global loads there would sit behind the previous float4's
+// stores (possible aliasing) and cost a memory round trip each.
 template <int NV>
 __global__ __launch_bounds__(256, NV <= 8 ? 4 : 2) void ln_modulate_kernel(
     const float* __restrict__ xin, int d_in, float* __restrict__ xout, const float* __restrict__ shift,
     const float* __restrict__ scale, uint16_t* __restrict__ h, int tokens, int d) {
+  __shared__ f32x4_t s_sh[NV * 64], s_sc[NV * 64];
   const int lane = threadIdx.x & 63;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (t >= tokens) return;
+  const int64_t t_raw = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const bool row_ok = t_raw < tokens;  // rows past the end compute on the last row and store nothing
+  const int64_t t = row_ok ? t_raw : tokens - 1;
   const float* xr = xin + t * d_in;
   const int nv = d / 4;
   const int lim = min(nv, d_in / 4);  // float4s of the row that come from xin
@@ -78,6 +85,10 @@ __global__ __launch_bounds__(256, NV <= 8 ? 4 : 2) void ln_modulate_kernel(
     v[i] = f32x4_t{in ? l.x : 0.f, in ? l.y : 0.f, in ? l.z : 0.f, in ? l.w : 0.f};
     s += v[i].x + v[i].y + v[i].z + v[i].w;
   }
+  for (int j = threadIdx.x; j < nv; j += 256) {
+    s_sh[j] = *reinterpret_cast<const f32x4_t*>(shift + j * 4);
+    s_sc[j] = *reinterpret_cast<const f32x4_t*>(scale + j * 4);
+  }
   const float mean = wave_sum(s) / static_cast<float>(d);
   float ss = 0.f;
 #pragma unroll
@@ -90,15 +101,13 @@ __global__ __launch_bounds__(256, NV <= 8 ? 4 : 2) void ln_modulate_kernel(
   }
   const float var = wave_sum(ss) / static_cast<float>(d);
   const float rstd = rsqrtf(var + 1e-6f);
+  __syncthreads();  // shift and scale staged
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int q = lane + i * 64;
-    // one float4 at a time: hoisting every shift/scale load would double
-    // the live registers
-    __builtin_amdgcn_sched_barrier(0);
-    if (q < nv) {
-      const f32x4_t sh = *reinterpret_cast<const f32x4_t*>(shift + q * 4);
-      const f32x4_t sc = *reinterpret_cast<const f32x4_t*>(scale + q * 4);
+    if (row_ok && q < nv) {
+      const f32x4_t sh = s_sh[q];
+      const f32x4_t sc = s_sc[q];
       const f32x4_t y = (v[i] - mean) * rstd * (1.0f + sc) + sh;
       u32x2_t o;
       o.x = pack_f16x2(y.x, y.y);
@@ -143,6 +152,14 @@ __global__ __launch_bounds__(THREADS) void ln_modulate_row_kernel(
     if (q < nv && q * 4 < d_in) v[i] = *reinterpret_cast<const f32x4_t*>(xr + q * 4);
     s += v[i].x + v[i].y + v[i].z + v[i].w;
   }
+  // shift and scale load with the row (before any store of this thread)
+  f32x4_t shv[NV], scv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int q = min(static_cast<int>(threadIdx.x) + i * THREADS, nv - 1);
+    shv[i] = *reinterpret_cast<const f32x4_t*>(shift + q * 4);
+    scv[i] = *reinterpret_cast<const f32x4_t*>(scale + q * 4);
+  }
   const float mean = block_sum<THREADS>(s, red) / static_cast<float>(d);
   float ss = 0.f;
 #pragma unroll
@@ -159,8 +176,8 @@ __global__ __launch_bounds__(THREADS) void ln_modulate_row_kernel(
   for (int i = 0; i < NV; ++i) {
     const int q = threadIdx.x + i * THREADS;
     if (q < nv) {
-      const f32x4_t sh = *reinterpret_cast<const f32x4_t*>(shift + q * 4);
-      const f32x4_t sc = *reinterpret_cast<const f32x4_t*>(scale + q * 4);
+      const f32x4_t sh = shv[i];
+      const f32x4_t sc = scv[i];
       const f32x4_t y = (v[i] - mean) * rstd * (1.0f + sc) + sh;
       u32x2_t o;
       o.x = pack_f16x2(y.x, y.y);
