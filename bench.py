@@ -426,8 +426,8 @@ def main():
                     "steady_state": steady},
         "residency": {"high_water_blocks": st["residency_high_water"],
                       "high_water_note": "most blocks whose slot was occupied at one instant (from the block's first "
-                                         "reconstruction write to the end of its compute); 1 when the host link "
-                                         "is the bottleneck, since block b+1 lands only after block b computed",
+                                         "reconstruction write to the end of its compute); 1 when each block "
+                                         "travels as one transfer that lands only after the previous block computed",
                       "slot_bytes": st["slot_bytes"],
                       "landing_bytes": st["landing_bytes"], "workspace_bytes": st["workspace_bytes"]},
         "kernels": kernels,
