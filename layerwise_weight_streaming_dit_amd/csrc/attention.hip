@@ -44,15 +44,20 @@ namespace dlo {
 
 namespace {
 
-constexpr int kAttnThreads = 512;
-constexpr int kBQ = 256;           // queries per workgroup (32 per wave)
 constexpr int kBKV = 64;           // keys per step
 constexpr float kRescaleSlack = 8.0f;  // log2 of the largest unnormalised probability
 
-template <int HD>
-__global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(
+// BQ queries per workgroup, 32 per wave: 256 (8 waves, one workgroup per
+// CU) normally; 128 (4 waves, two workgroups per CU) when 256-query tiles
+// would leave CUs idle (short sequences: T 1000, 4 heads runs in 16 instead
+// of 24 us), since with enough tiles the larger tile is faster (T 4096: 154
+// vs 175 us).
+template <int HD, int BQ>
+__global__ __launch_bounds__(BQ * 2, BQ == 256 ? 1 : 2) void attention_kernel(
     const uint16_t* __restrict__ qk, int ld_qk, const uint16_t* __restrict__ vt, int ld_vt,
     uint16_t* __restrict__ o, int ld_o, int T, int H, float scale_log2) {
+  constexpr int kAttnThreads = BQ * 2;  // 64 lanes per 32 queries
+  constexpr int kBQ = BQ;
   constexpr int KCH = HD / 8;           // 16-byte chunks per K row
   // 16-byte chunk swizzles, so that the 16 lanes the LDS serves together
   // (16 consecutive rows, same logical chunk) hit 16 distinct 16-byte bank
@@ -254,14 +259,21 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attention_kernel(
 hipError_t launch_attention(const uint16_t* qk, int ld_qk, const uint16_t* vt, int ld_vt, uint16_t* o,
                             int ld_o, int tokens, int heads, int head_dim, hipStream_t s) {
   if (tokens <= 0) return hipSuccess;
-  const dim3 grid(((tokens + kBQ - 1) / kBQ) * heads), block(kAttnThreads);
   const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(head_dim)));
-  if (head_dim == 128)
-    hipLaunchKernelGGL(attention_kernel<128>, grid, block, 0, s, qk, ld_qk, vt, ld_vt, o, ld_o, tokens,
-                       heads, scale_log2);
-  else
-    hipLaunchKernelGGL(attention_kernel<64>, grid, block, 0, s, qk, ld_qk, vt, ld_vt, o, ld_o, tokens,
-                       heads, scale_log2);
+  // 256-query tiles unless they would leave some of the 256 CUs idle
+  const bool small = static_cast<int64_t>((tokens + 255) / 256) * heads < 256;
+  const int bq = small ? 128 : 256;
+  const dim3 grid(((tokens + bq - 1) / bq) * heads), block(bq * 2);
+#define DLO_ATTN(HD, BQ) \
+  hipLaunchKernelGGL((attention_kernel<HD, BQ>), grid, block, 0, s, qk, ld_qk, vt, ld_vt, o, ld_o, tokens, heads, scale_log2)
+  if (head_dim == 128) {
+    if (small) DLO_ATTN(128, 128);
+    else DLO_ATTN(128, 256);
+  } else {
+    if (small) DLO_ATTN(64, 128);
+    else DLO_ATTN(64, 256);
+  }
+#undef DLO_ATTN
   return hipGetLastError();
 }
 
