@@ -177,6 +177,7 @@ def test_gemm_large_tile_shapes():
 
 @pytest.mark.parametrize("epi,M,N,K", [(dlo.EPI_BIAS_F16, 4000, 2048, 4096), (dlo.EPI_GATED_F32, 4000, 2048, 4096),
                                          (dlo.EPI_VT_F16, 4000, 2048, 4096), (dlo.EPI_BIAS_GELU_F16, 4000, 2048, 4096),
+                                         (dlo.EPI_GATED_F32, 4000, 2000, 4096), (dlo.EPI_BIAS_F16, 4000, 2000, 4096),
                                          (dlo.EPI_BIAS_F16, 4096 + 17, 4096, 1024),
                                          (dlo.EPI_GATED_F32, 4096 + 17, 4096, 1024),
                                          (dlo.EPI_BIAS_GELU_F16, 4096 + 17, 4096 - 48, 1024),
@@ -254,6 +255,36 @@ def test_attention_heads_per_xcd(T, H, hd):
     got, want = _attention_case(T, H, hd, seed=T + H)
     ok, ma, mr = within(got, want, rtol=5e-3, atol=5e-3)
     assert ok, (ma, mr)
+
+
+@pytest.mark.parametrize("T,H,hd", [(4096, 20, 64), (2048 + 33, 32, 128)])
+def test_attention_full_grid_sampled_queries(T, H, hd):
+    """Sequences long enough for 256-query tiles (one workgroup per CU),
+    with a head count that is not a multiple of 8 (plain grid order) and one
+    that is (heads kept on one XCD), ragged last key tile included; checked
+    on sampled query rows against fp64 softmax attention over all keys."""
+    rng = np.random.default_rng(T + H + hd)
+    d = H * hd
+    q = _f16(rng.standard_normal((T, d)))
+    k = _f16(rng.standard_normal((T, d)))
+    v = _f16(rng.standard_normal((T, d)))
+    tp = (T + 63) // 64 * 64
+    vt = np.zeros((d, tp), np.uint16)
+    vt[:, vt_position(np.arange(T))] = v.T
+    t = torch()
+    o = t.empty((T, d), dtype=t.int16, device="cuda")
+    dlo.op_attention(dev(np.concatenate([q, k], axis=1)), 2 * d, dev(vt), tp, o, d, T, H, hd)
+    got = f16_to_f64(host(o, np.uint16))
+    rows = np.unique(np.concatenate([rng.choice(T, 24, replace=False), [0, T - 1]]))
+    qf, kf, vf = f16_to_f64(q), f16_to_f64(k), f16_to_f64(v)
+    want = np.empty((len(rows), d))
+    for h in range(H):
+        c = slice(h * hd, (h + 1) * hd)
+        sc = qf[rows, c] @ kf[:, c].T / np.sqrt(hd)
+        p = np.exp(sc - sc.max(axis=1, keepdims=True))
+        want[:, c] = (p / p.sum(axis=1, keepdims=True)) @ vf[:, c]
+    ok, ma, mr = within(got[rows], want, rtol=5e-3, atol=5e-3)
+    assert ok, (T, H, hd, ma, mr)
 
 
 @pytest.mark.parametrize("qscale", [4.0, 30.0])
