@@ -64,9 +64,9 @@ DLO_API dlo_status dlo_op_ln_modulate(const float* xin, int32_t d_in, float* xou
  * where p(j) swaps bits 2 and 3 of j (the transposed v layout attention
  * reads, see dlo_op_attention).  bias is bf16, gate fp32.  M >= 1; N a
  * multiple of 16; K a multiple of 128; lda, ldw multiples of 8 and >= K;
- * ldo a multiple of 4 and >= N; 1 <= w_rows <= N; a, w 16-byte aligned, out
- * 8-byte (16 for the fp32 epilogue), bias 8-byte (column bias), gate
- * 16-byte. */
+ * ldo >= N and a multiple of 8 (of 4 for the fp32 epilogue), so that every
+ * output row starts 16-byte aligned; 1 <= w_rows <= N; a, w and out 16-byte
+ * aligned, bias 8-byte (column bias), gate 16-byte. */
 #define DLO_EPI_BIAS_F16 0
 #define DLO_EPI_BIAS_GELU_F16 1
 #define DLO_EPI_GATED_F32 2

@@ -67,13 +67,15 @@ extern "C" DLO_API dlo_status dlo_op_gemm(int32_t epilogue, const uint16_t* a, i
     return fail(DLO_E_SHAPE, "M %d, N %d, K %d (N a multiple of 16, K of 128)", M, N, K);
   if (w_rows < 1 || w_rows > N) return fail(DLO_E_SHAPE, "w_rows %d outside [1, N=%d]", w_rows, N);
   if (lda < K || ldw < K || lda % 8 || ldw % 8) return fail(DLO_E_SHAPE, "lda %d / ldw %d must be >= K and multiples of 8", lda, ldw);
-  if (ldo < N || ldo % 4) return fail(DLO_E_SHAPE, "ldo %d must be >= N %d and a multiple of 4", ldo, N);
+  // the epilogue writes 16-byte row pieces: 8 fp16 or 4 fp32 columns
+  const int ldo_mult = epilogue == DLO_EPI_GATED_F32 ? 4 : 8;
+  if (ldo < N || ldo % ldo_mult)
+    return fail(DLO_E_SHAPE, "ldo %d must be >= N %d and a multiple of %d", ldo, N, ldo_mult);
   // the kernel addresses both operands with 32-bit byte offsets
   if ((int64_t(M - 1) * lda + K) * 2 > int64_t(UINT32_MAX) || (int64_t(w_rows - 1) * ldw + K) * 2 > int64_t(UINT32_MAX))
     return fail(DLO_E_SHAPE, "operand extent beyond 4 GiB (M %d x lda %d, w_rows %d x ldw %d)", M, lda, w_rows, ldw);
   if (!aligned(a, 16) || !aligned(w, 16)) return fail(DLO_E_INVAL, "operands must be 16-byte aligned");
-  const size_t oal = epilogue == DLO_EPI_GATED_F32 ? 16 : 8;
-  if (!aligned(out, oal) || !aligned(bias, epilogue == DLO_EPI_VT_F16 ? 2 : 8) ||
+  if (!aligned(out, 16) || !aligned(bias, epilogue == DLO_EPI_VT_F16 ? 2 : 8) ||
       (gate && !aligned(gate, 16)))
     return fail(DLO_E_INVAL, "out, bias or gate misaligned for vector access");
   GemmArgs g{a, w, bias, gate, out, lda, ldw, ldo, M, N, K, w_rows};

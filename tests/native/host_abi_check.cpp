@@ -209,6 +209,10 @@ void check_gemm() {
       {0, 128, 128, 16, 12, 1, 16, 128, 0x100000, 0x500000},           // ldo < N
       {0, 128, 128, 16, 16, 1, 16, 128, 0x100008, 0x500000},           // a not 16-byte aligned
       {2, 128, 128, 16, 16, 1, 16, 128, 0x100000, 0x500008},           // fp32 out not 16-byte aligned
+      {0, 128, 128, 16, 16, 1, 16, 128, 0x100000, 0x500008},           // fp16 out not 16-byte aligned
+      {3, 128, 128, 16, 16, 1, 16, 128, 0x100000, 0x500008},           // transposed out not 16-byte aligned
+      {0, 128, 128, 16, 20, 1, 16, 128, 0x100000, 0x500000},           // fp16 ldo not a multiple of 8
+      {1, 128, 128, 16, 20, 1, 16, 128, 0x100000, 0x500000},           // GELU ldo not a multiple of 8
       {0, 16384, 128, 16, 16, (1 << 17) + 1, 16, 128, 0x100000, 0x500000},  // a beyond 4 GiB
   };
   for (auto& c : cases) {
@@ -219,6 +223,10 @@ void check_gemm() {
     CHECK(g_seen.calls == 0);
     CHECK(has_error_text());
   }
+  // fp32 rows need only 4-column strides (16 bytes)
+  g_seen = Seen{};
+  CHECK(dlo_op_gemm(DLO_EPI_GATED_F32, a, 128, w, 128, 16, bias, gate, out, 20, 1, 16, 128, nullptr) == DLO_OK);
+  CHECK(g_seen.calls == 1 && g_seen.gemm.ldo == 20);
   // the largest operand that still fits 32-bit offsets is accepted
   g_seen = Seen{};
   CHECK(dlo_op_gemm(0, a, 16384, w, 128, 16, bias, nullptr, out, 16, 1 << 17, 16, 128, nullptr) == DLO_OK);

@@ -65,10 +65,28 @@ def test_adaln(d, c):
     assert ok, (ma, mr)
 
 
+@pytest.mark.parametrize("rows,c", [(1, 64), (17, 320), (1003, 4096), (4099, 256)])
+def test_adaln_ragged_rows(rows, c):
+    # row counts that leave a workgroup's last rows empty (16 rows per
+    # workgroup, 4 per wave) and widths from one lane group to the LDS limit
+    rng = np.random.default_rng(rows * 7 + c)
+    w = _bf16(rng.standard_normal((rows, c)) * 0.02)
+    b = _bf16(rng.standard_normal(rows) * 0.02)
+    cond = rng.standard_normal(c).astype(np.float32)
+    mod = dev(np.full(rows + 16, np.nan, np.float32))
+    dlo.op_adaln(dev(w), dev(b), dev(cond), mod, rows, c)
+    got = host(mod)
+    want = bf16_to_f64(w).reshape(rows, c) @ D.silu(cond.astype(np.float64)) + bf16_to_f64(b)
+    ok, ma, mr = within(got[:rows], want, rtol=1e-4, atol=1e-5)
+    assert ok, (ma, mr)
+    assert np.all(np.isnan(got[rows:])), "wrote past the last row"
+
+
 # ------------------------------------------------------- LayerNorm + modulate
 
 @pytest.mark.parametrize("tokens,d_in,d", [(1, 256, 256), (37, 2048, 2048), (300, 3072, 4096),
-                                           (65, 4096, 3072), (8, 8192, 8192)])
+                                           (65, 4096, 3072), (8, 8192, 8192), (5, 8, 4), (17, 1000, 1024),
+                                           (6, 516, 500), (3, 4100, 6000), (2, 6000, 4100)])
 def test_ln_modulate(tokens, d_in, d):
     rng = np.random.default_rng(tokens * d)
     x = (rng.standard_normal((tokens, d_in)) * 2 + 0.5).astype(np.float32)
@@ -88,10 +106,25 @@ def test_ln_modulate(tokens, d_in, d):
 
 # --------------------------------------------------------------------- GEMM
 
-def _gemm_case(epi, M, N, K, w_rows=None, seed=0):
+_POISON = 0x7FFF  # NaN as fp16 and as bf16
+_SENTINEL_F16, _SENTINEL_F32 = 0x1234, 12345.0
+
+
+def _padded(rows_bits, ld):
+    """rows_bits (uint16 [rows][cols]) in a [rows][ld] buffer whose padding is NaN."""
+    buf = np.full((rows_bits.shape[0], ld), _POISON, np.uint16)
+    buf[:, : rows_bits.shape[1]] = rows_bits
+    return buf
+
+
+def _gemm_case(epi, M, N, K, w_rows=None, seed=0, pad=None):
     """One GEMM through the C ABI; `a` is the fp16 activation and `w` the
-    bf16 weight, except for the transposed-v epilogue where the roles swap."""
+    bf16 weight, except for the transposed-v epilogue where the roles swap.
+    pad = (extra lda, extra ldw, extra ldo): the operands' row padding holds
+    NaN (a read of it would poison the result) and the output's a sentinel
+    that must survive."""
     rng = np.random.default_rng(seed)
+    pa, pw, po = pad or (0, 0, 0)
     w_rows = N if w_rows is None else w_rows
     vt = epi == dlo.EPI_VT_F16
     a_val = rng.standard_normal((M, K)) * (0.02 if vt else 1.0)
@@ -102,12 +135,18 @@ def _gemm_case(epi, M, N, K, w_rows=None, seed=0):
     bias = _bf16(rng.standard_normal(nb) * 0.1)
     gate = rng.standard_normal(N).astype(np.float32)
     x0 = rng.standard_normal((M, N)).astype(np.float32)
-    t = torch()
     if epi == dlo.EPI_GATED_F32:
-        out = dev(x0.copy())
+        out_h = np.full((M, N + po), _SENTINEL_F32, np.float32)
+        out_h[:, :N] = x0
     else:
-        out = t.empty((M, N), dtype=t.int16, device="cuda")
-    dlo.op_gemm(epi, dev(a), K, dev(w), K, w_rows, dev(bias), dev(gate), out, N, M, N, K)
+        out_h = np.full((M, N + po), _SENTINEL_F16, np.uint16)
+    out = dev(out_h)
+    dlo.op_gemm(epi, dev(_padded(a, K + pa)), K + pa, dev(_padded(w, K + pw)), K + pw, w_rows, dev(bias),
+                dev(gate), out, N + po, M, N, K)
+    if po:
+        got_all = host(out) if epi == dlo.EPI_GATED_F32 else host(out, np.uint16)
+        assert np.array_equal(got_all[:, N:], out_h[:, N:]), "output padding was written"
+        out = out[:, :N]
     wf = f16_to_f64(w) if vt else bf16_to_f64(w)
     wfull = wf[np.minimum(np.arange(N), w_rows - 1)]
     acc = (bf16_to_f64(a) if vt else f16_to_f64(a)) @ wfull.T
@@ -134,6 +173,18 @@ def test_gemm(epi, M, N, K):
 def test_gemm_clamped_w_rows():
     # the transposed v projection: output columns past w_rows repeat the last row
     got, want = _gemm_case(dlo.EPI_VT_F16, 512, 1088, 256, w_rows=1000, seed=5)
+    ok, ma, mr = within(got, want, rtol=2e-3, atol=2e-3)
+    assert ok, (ma, mr)
+
+
+@pytest.mark.parametrize("epi", [dlo.EPI_BIAS_F16, dlo.EPI_BIAS_GELU_F16, dlo.EPI_GATED_F32, dlo.EPI_VT_F16])
+@pytest.mark.parametrize("M,N,K", [(300, 272, 256), (4096 + 40, 2048, 4096)])
+def test_gemm_strided_operands(epi, M, N, K):
+    # row strides past the logical extents: lda = K + 8, ldw = K + 24 and
+    # ldo = N + 8 (N + 4 for fp32 rows); the second shape takes the 256x128
+    # tiles with the L2 prefetch and a ragged last tile row
+    po = 4 if epi == dlo.EPI_GATED_F32 else 8
+    got, want = _gemm_case(epi, M, N, K, seed=M + K + epi, pad=(8, 24, po))
     ok, ma, mr = within(got, want, rtol=2e-3, atol=2e-3)
     assert ok, (ma, mr)
 
