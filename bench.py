@@ -322,7 +322,7 @@ def main():
         work = sum(kernel_work(shapes[r["block"]], T)[kind][1] for r in rs) / len(rs)
         rate = work / (avg * 1e-3)
         # the median shows how far a few slow launches pull the average
-        e = {"launches": len(rs), "avg_ms": avg, "median_ms": ds[len(ds) // 2], "total_ms": dur(rs),
+        e = {"launches": len(rs), "avg_ms": avg, "median_ms": ds[len(ds) // 2], "max_ms": ds[-1], "total_ms": dur(rs),
              "work_per_launch": work, "desc": KERNEL_DESC[kind]}
         if unit == "flop":
             e["TFLOPs"] = rate / 1e12
@@ -346,6 +346,10 @@ def main():
                 "frac": ach / (PEAK_BF16_TFLOPS if unit == "flop" else PEAK_HBM_GBPS),
                 "traffic": traffic_from_profiles(src, dom, wl.name),
                 "kernel": f"{dom}: {KERNEL_DESC[dom]}", "avg_launch_ms": kernels[dom]["avg_ms"],
+                # achieved and frac use the average launch; a single launch
+                # caught in one of the device's occasional multi-millisecond
+                # stalls moves it, the median does not
+                "median_launch_ms": kernels[dom]["median_ms"], "max_launch_ms": kernels[dom]["max_ms"],
                 "work_per_launch": work, "work_unit": unit}
 
     # synchronous schedule (H2D -> wait -> reconstruct -> wait -> compute), same kernels
