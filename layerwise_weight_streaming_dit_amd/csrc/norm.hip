@@ -55,7 +55,8 @@ __global__ __launch_bounds__(kNormThreads) void adaln_kernel(const uint16_t* __r
 // d) is held in registers, NV float4 per lane (NV * 256 >= d), so mean and
 // variance are wave reductions with no LDS or barrier, and every lane has NV
 // loads in flight.  The register cap keeps 4 waves per SIMD resident for
-// d <= 2048, 2 up to 4096; wider rows use the workgroup-per-row kernel below.
+// d <= 2048, 2 up to 6144 (d = 6144 needs 232 registers and no spills);
+// wider rows use the workgroup-per-row kernel below.
 //
 // shift and scale are shared by the workgroup's four rows: they are staged in
 // LDS once (their loads overlap the rows' loads), so the output loop reads
@@ -131,7 +132,7 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
-// Wide rows (d > 4096): one workgroup per token row.  The row (adapted to
+// Wide rows (d > 6144): one workgroup per token row.  The row (adapted to
 // width d) is held in registers, at most two float4 per thread (1024 threads
 // for d = 8192, so registers stay few and occupancy high); mean and variance
 // are workgroup reductions over the registers.
@@ -209,6 +210,7 @@ hipError_t launch_ln_modulate(const float* xin, int d_in, float* xout, const flo
   else if (d <= 1024) DLO_LN(4);
   else if (d <= 2048) DLO_LN(8);
   else if (d <= 4096) DLO_LN(16);
+  else if (d <= 6144) DLO_LN(24);
   else
     hipLaunchKernelGGL((ln_modulate_row_kernel<1024, 2>), dim3(tokens), dim3(1024), 0, s, xin, d_in, xout, shift,
                        scale, h, d);

@@ -86,7 +86,8 @@ def test_adaln_ragged_rows(rows, c):
 
 @pytest.mark.parametrize("tokens,d_in,d", [(1, 256, 256), (37, 2048, 2048), (300, 3072, 4096),
                                            (65, 4096, 3072), (8, 8192, 8192), (5, 8, 4), (17, 1000, 1024),
-                                           (6, 516, 500), (3, 4100, 6000), (2, 6000, 4100)])
+                                           (6, 516, 500), (3, 4100, 6000), (2, 6000, 4100),
+                                           (129, 5120, 5120), (5, 6144, 6144), (3, 6148, 6148)])
 def test_ln_modulate(tokens, d_in, d):
     rng = np.random.default_rng(tokens * d)
     x = (rng.standard_normal((tokens, d_in)) * 2 + 0.5).astype(np.float32)
