@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the layer-by-layer weight-streamed DiT forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload image]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large]
 
 A step is one streamed forward over every block of the workload (H2D of all
 dp shards of every block, on-GPU reconstruction into one of two slots, and
@@ -9,10 +9,17 @@ the DiT block from the other slot), for one batch of synthetic input whose
 weights already sit in pinned host memory and whose activations already sit
 in HBM.  W untimed steps, then K timed steps between two device syncs.
 
+The default workload is the largest one: 80 blocks of d 8192 (about 131 GB of
+bf16 weights, held only in pinned host memory).  Its weights are drawn block by
+block and handed to the library, which copies them into its pinned shards, so
+host memory holds the model once.  One pinned shard store serves every pass:
+the timed forwards, an untraced pass, a fully traced pass over two
+consecutive forwards and a serialized pass (dlo_set_flags between them).
+
 Prints ONE JSON line: blocks/s as ``value`` plus tokens/s, H2D GB/s, GEMM
-MFMA utilisation, overlap, a roofline of the dominant kernel (timed with HIP
-events on the compute stream inside the timed region) and the oracle timed
-on the host cores.
+MFMA utilisation, overlap, per-step overheads, device weight residency, a
+roofline of the dominant kernel (timed with HIP events on the compute stream
+inside the timed region) and the oracle timed on the host cores.
 """
 from __future__ import annotations
 
@@ -39,6 +46,13 @@ KERNEL_DESC = {
     "k_fc2": "MLP down GEMM + gated residual", "k_adaln": "adaLN GEMV", "k_ln1": "LayerNorm+modulate",
     "k_ln2": "LayerNorm+modulate",
 }
+# pages' per-step overhead of the all-gather mode (release page, "Validation":
+# Ascend 910B3, Cosmos3-Nano, DP4): stream switching and Python dispatch
+PAGES_STEP_OVERHEAD_MS = {"stream_switching": 72.0, "collective_calls": 10.0, "python_dispatch": 68.0}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def kernel_work(shape, T):
@@ -86,31 +100,93 @@ def source_hash(path):
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kernel_src, kind, workload):
+def kernel_source(kind):
+    unit = "flop" if kind in ("k_qk", "k_v", "k_attn", "k_out", "k_fc1", "k_fc2") else "byte"
+    name = "attention.hip" if kind == "k_attn" else ("gemm.hip" if unit == "flop" else "norm.hip")
+    return os.path.join(ROOT, "layerwise_weight_streaming_dit_amd", "csrc", name)
+
+
+def traffic_from_profiles(kind, workload):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter
-    summary (profiles/hbm_traffic_image_dit.txt: lines "kind source-sha16
-    fetch-bytes write-bytes", copy-calibrated), used only for the workload the
-    counters were taken on (image) and only if they were taken on the current
-    kernel source and device headers; else None."""
-    if workload != "image":
-        return None
-    p = os.path.join(ROOT, "profiles", "hbm_traffic_image_dit.txt")
+    summary of this workload (profiles/hbm_traffic_<workload>_dit.txt: lines
+    "kind source-sha16 fetch-bytes write-bytes", copy-calibrated), only if
+    the counters were taken on the current kernel source and device headers;
+    else None."""
+    p = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}_dit.txt")
     if not os.path.exists(p):
         return None
-    want = source_hash(kernel_src)
+    want = source_hash(kernel_source(kind))
+    alias = {"k_ln1": "k_ln", "k_ln2": "k_ln"}.get(kind, kind)
     for line in open(p):
         f = line.split()
-        if len(f) == 4 and f[0] == kind and f[1] == want:
+        if len(f) == 4 and f[0] == alias and f[1] == want:
             return float(f[2]) + float(f[3])
     return None
 
 
-def cpu_baseline(wl, dp, T, seconds):
+def busy(rs):
+    """Length of the union of intervals (the two copy engines overlap)."""
+    tot, cs, ce = 0.0, None, None
+    for r in sorted(rs, key=lambda r: r["start"]):
+        if ce is None or r["start"] > ce:
+            if ce is not None:
+                tot += ce - cs
+            cs, ce = r["start"], r["end"]
+        else:
+            ce = max(ce, r["end"])
+    return tot + (ce - cs if ce is not None else 0.0)
+
+
+def overlap_of(rs):
+    """Overlap figures of the intervals of one forward: E = max(busy(H2D and
+    reconstruction), busy(compute)) / t_forward (<= 1; 1 = the slower side
+    never waits), and the hidden fraction (H2D + compute - t) / min of the
+    two (1 = the faster side is entirely hidden behind the slower)."""
+    stage = [r for r in rs if r["kind"] in ("h2d", "asm")]
+    comp = [r for r in rs if r["kind"] == "compute"]
+    t = max(r["end"] for r in rs) - min(r["start"] for r in rs)
+    h, a, c, st = (busy([r for r in rs if r["kind"] == "h2d"]), busy([r for r in rs if r["kind"] == "asm"]),
+                   busy(comp), busy(stage))
+    return {"t_forward_ms": t, "sum_h2d_ms": h, "sum_asm_ms": a, "sum_compute_ms": c,
+            "E": max(st, c) / t, "hidden_frac": (h + c - t) / min(h, c),
+            "hidden_side": "compute behind H2D" if c < h else "H2D behind compute"}
+
+
+def step_costs(tr, L, f):
+    """Per-step costs of forward f in a trace spanning forwards f-1 and f:
+    the compute stream's idle time between consecutive blocks, split into the
+    wait for a block's weights (its reconstruction ended after the previous
+    block's compute) and the switch itself (event wait + launch after the
+    weights were ready), and the step time (last compute end to last compute
+    end)."""
+    comp = {(r["forward"], r["block"]): r for r in tr if r["kind"] == "compute"}
+    ready = {}
+    for r in tr:
+        if r["kind"] == "asm":
+            k = (r["forward"], r["block"])
+            ready[k] = max(ready.get(k, r["end"]), r["end"])
+    wait = switch = boundary = 0.0
+    for b in range(L):
+        prev = comp[(f, b - 1)] if b > 0 else comp[(f - 1, L - 1)]
+        cur = comp[(f, b)]
+        rdy = ready[(f, b)]
+        w = max(0.0, rdy - prev["end"])
+        sw = max(0.0, cur["start"] - max(prev["end"], rdy))
+        wait += w
+        switch += sw
+        if b == 0:
+            boundary = cur["start"] - prev["end"]
+    return {"step_ms": comp[(f, L - 1)]["end"] - comp[(f - 1, L - 1)]["end"],
+            "compute_idle_waiting_for_weights_ms": wait, "stream_switch_ms": switch,
+            "step_boundary_gap_ms": boundary}
+
+
+def cpu_baseline(wl, shapes, T, W_keep, seconds, min_blocks):
     """The oracle timed on the host cores on a bounded sample of blocks of the
-    same workload at the full token count; blocks/s = blocks run / elapsed.
-    `value` runs the oracle's arithmetic in fp32 (numpy with every BLAS
-    thread); the same oracle at its default fp64 is timed on a smaller
-    sample and reported beside it."""
+    same workload at the full token count; blocks/s = blocks run / elapsed
+    (a full forward would take blocks / value seconds).  `value` runs the
+    oracle's arithmetic in fp32 (numpy with every BLAS thread); the oracle at
+    its default fp64 is timed beside it where a block fits half the budget."""
     import numpy as np
     import synth
     from oracle import dit as D, layout as OL
@@ -120,47 +196,55 @@ def cpu_baseline(wl, dp, T, seconds):
     except Exception:
         threads = 0
 
-    def timed(dtype, budget):
-        x = synth.activations(T, wl.blocks[0].d_model)
-        cond = synth.conditioning(wl.blocks[0].d_cond)
+    def timed(dtype, budget, at_least):
+        x = synth.activations(T, shapes[0].d_model)
+        cond = synth.conditioning(shapes[0].d_cond)
         n, elapsed = 0, 0.0
-        for b in range(wl.num_blocks):
-            shp = wl.blocks[b]
-            flat = synth.block_weights(wl.wid, b, OL.block_numel(shp))
+        for b in range(len(shapes)):
+            shp = shapes[b]
+            flat = W_keep[b] if b in W_keep else synth.block_weights(wl.wid, b, OL.block_numel(shp))
             if x.shape[1] != shp.d_model:
                 x = D.width_adapter(x, shp.d_model)
             ts = time.perf_counter()
             x = D.dit_block(flat, shp, x, cond, dtype=dtype)
             elapsed += time.perf_counter() - ts
             n += 1
-            if elapsed >= budget:
+            log(f"cpu baseline ({np.dtype(dtype).name}): block {b} in {time.perf_counter() - ts:.1f} s")
+            if elapsed >= budget and n >= at_least:
                 break
         return n, elapsed
 
-    n, elapsed = timed(np.float32, seconds)
-    n64, el64 = timed(np.float64, seconds / 2)
+    n, elapsed = timed(np.float32, seconds, min_blocks)
     bps = n / elapsed
-    return {"value": bps, "unit": "blocks/s", "cores": threads or os.cpu_count(), "kind": "oracle",
-            "sample": f"{n} of {wl.num_blocks} blocks of the {wl.name} workload at T={T}, numpy fp32, "
-                      f"{elapsed:.1f} s of block compute (weight generation not timed)",
-            "tokens_per_s": bps * T / wl.num_blocks,
-            "fp64": {"value": n64 / el64, "unit": "blocks/s",
-                     "sample": f"{n64} of {wl.num_blocks} blocks, numpy fp64 (the oracle's default), {el64:.1f} s"}}
+    out = {"value": bps, "unit": "blocks/s", "cores": threads or os.cpu_count(), "kind": "oracle",
+           "sample": f"{n} of {len(shapes)} blocks of the {wl.name} workload at T={T}, numpy fp32, "
+                     f"{elapsed:.1f} s of block compute (weight generation not timed); a whole "
+                     f"{len(shapes)}-block forward extrapolates to {len(shapes) / bps:.0f} s",
+           "tokens_per_s": bps * T / len(shapes)}
+    if elapsed / n <= seconds / 2:
+        n64, el64 = timed(np.float64, seconds / 2, 1)
+        out["fp64"] = {"value": n64 / el64, "unit": "blocks/s",
+                       "sample": f"{n64} of {len(shapes)} blocks, numpy fp64 (the oracle's default), {el64:.1f} s"}
+    return out
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="image")
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="large")
     ap.add_argument("--dp", type=int, default=0)
     ap.add_argument("--blocks", type=int, default=0,
-                    help="stream only the first N blocks of the workload (per-block rates unchanged; "
-                         "for shapes whose full weight set would not fit host memory twice)")
+                    help="stream only the first N blocks of the workload (per-block rates unchanged)")
+    ap.add_argument("--chunk", type=int, default=0, help="H2D chunk in elements (0 = the library's default)")
+    ap.add_argument("--gen-threads", type=int, default=12)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-min-blocks", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-serial", action="store_true")
+    ap.add_argument("--timed-only", action="store_true",
+                    help="only the warm-up and timed forwards (for counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device copy (the reconstruction kernel) so "
                          "a counter pass can scale HBM byte counters by a copy of known size")
@@ -186,7 +270,7 @@ def main():
         torch.cuda.synchronize()
         dlo.op_assemble(dst, src, n)
         torch.cuda.synchronize()
-        print(f"[bench] calibration copy: {2 * n} bytes read, {2 * n} bytes written", file=sys.stderr, flush=True)
+        log(f"calibration copy: {2 * n} bytes read, {2 * n} bytes written")
         del src, dst
     wl = synth.workload(args.workload)
     shapes = list(wl.blocks)[: args.blocks] if args.blocks > 0 else list(wl.blocks)
@@ -194,17 +278,47 @@ def main():
     T = wl.tokens
     L = len(shapes)
     dev = torch.device("cuda:0")
+    numels = [dlo.block_layout(s, dp)[0] for s in shapes]
+    n_keep = 0 if args.no_cpu_baseline else min(args.cpu_min_blocks, L)
+
+    # ---- weights: drawn block by block and sharded into pinned memory; the
+    # library keeps no reference to the drawn array, so host memory holds the
+    # model once (plus the blocks drawn ahead)
+    def load(nblocks):
+        c = dlo.StreamedDiT(shapes[:nblocks], dp, T, flags=dlo.FLAG_TRACE_KERNELS, chunk_elems=args.chunk)
+        keep, t_gen = {}, time.perf_counter()
+        for b, flat in synth.iter_block_weights(wl.wid, numels[:nblocks], threads=args.gen_threads):
+            try:
+                c.load_shards(b, flat)
+            except dlo.DloError as e:
+                if e.code != dlo.E_HOST_OOM:
+                    raise
+                c.close()
+                return None, b, keep
+            if b < n_keep:
+                keep[b] = flat
+            if b % 10 == 9 or b == nblocks - 1:
+                log(f"{b + 1}/{nblocks} blocks drawn and pinned ({time.perf_counter() - t_gen:.1f} s)")
+        return c, nblocks, keep
 
     t0 = time.perf_counter()
-    numels = [dlo.block_layout(s, dp)[0] for s in shapes]
-    W = synth.many_block_weights(wl.wid, numels)
-    gen_s = time.perf_counter() - t0
-
-    def make(flags):
-        ctx = dlo.StreamedDiT(shapes, dp, T, flags=flags)
-        for b in range(L):
-            ctx.load_shards(b, W[b])
-        return ctx
+    ctx, loaded, W_keep = load(L)
+    repeats, note = 1, ""
+    if ctx is None:
+        # the host could not pin the whole model: stream a cyclic subset of k
+        # distinct blocks, L / k forwards of the k-block context per step
+        # (per-block H2D and compute are unchanged; the alternation continues
+        # across forwards)
+        k = max(d for d in range(1, L + 1) if L % d == 0 and d <= max(1, loaded - 2))
+        log(f"pinning failed after {loaded} blocks: streaming a cyclic subset of {k} blocks")
+        ctx, _, W_keep = load(k)
+        repeats = L // k
+        note = (f"; pinned host memory held only {loaded} of {L} blocks, so each step streams a cyclic "
+                f"subset of {k} distinct blocks {repeats} times ({L} block-steps)")
+    load_s = time.perf_counter() - t0
+    pinned_bytes = sum(2 * dp * (-(-n // dp)) for n in numels[: len(ctx.shapes)])
+    log(f"{wl.name}: {L} blocks, T={T}, dp={dp}; drawn, sharded and pinned in {load_s:.1f} s "
+        f"({pinned_bytes / 1e9:.1f} GB pinned)")
 
     x0 = torch.from_numpy(synth.activations(T, shapes[0].d_model).reshape(-1)).to(dev)
     xbuf = torch.zeros(T * max(s.d_model for s in shapes), dtype=torch.float32, device=dev)
@@ -212,124 +326,55 @@ def main():
     cond = torch.from_numpy(synth.conditioning(shapes[0].d_cond)).to(dev)
     stream = torch.cuda.current_stream()
 
-    t1 = time.perf_counter()
-    # the timed context records HIP events only on the compute stream (around
-    # each kernel), so the copy and gather streams run exactly as untraced
-    ctx = make(dlo.FLAG_TRACE_KERNELS)
-    load_s = time.perf_counter() - t1
-    print(f"[bench] {wl.name}: {L} blocks, T={T}, dp={dp}; weights generated in {gen_s:.1f} s, "
-          f"sharded+pinned in {load_s:.1f} s", file=sys.stderr, flush=True)
+    def step():
+        for _ in range(repeats):
+            ctx.forward(xbuf, cond, T)
 
-    for _ in range(args.warmup):
-        ctx.forward(xbuf, cond, T)
-    torch.cuda.synchronize()
+    # ---- timed region: HIP events only on the compute stream (around each
+    # kernel), created before timing starts
+    ctx.reserve_trace((args.warmup + args.steps) * repeats)
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warm-up step {i + 1}/{args.warmup} done")
     ctx.trace()  # kernel intervals accumulate until read: drop the warm-up's
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ts = time.perf_counter()
-    enqueue_s = 0.0
     ev0.record(stream)
     for _ in range(args.steps):
-        te = time.perf_counter()
-        ctx.forward(xbuf, cond, T)
-        enqueue_s += time.perf_counter() - te
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - ts
-    ev_ms = ev0.elapsed_time(ev1)
-    elapsed = wall
+    elapsed = time.perf_counter() - ts
     ms_per_step = 1e3 * elapsed / args.steps
-    print(f"[bench] timed {args.steps} forwards: {ms_per_step:.3f} ms/forward (events {ev_ms / args.steps:.3f})",
-          file=sys.stderr, flush=True)
-
-    # kernel durations: every launch of the timed region
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (events {ev0.elapsed_time(ev1) / args.steps:.3f})")
     ktr = ctx.trace()
-    # one forward on an idle device (no previous forward to overlap its
-    # pipeline fill with): the difference to the back-to-back step time is
-    # what streaming across step boundaries hides
-    iso = []
-    for _ in range(3):
-        torch.cuda.synchronize()
-        ti = time.perf_counter()
-        ctx.forward(xbuf, cond, T)
-        torch.cuda.synchronize()
-        iso.append(1e3 * (time.perf_counter() - ti))
-    iso_ms = sorted(iso)[1]
-    ctx.close()
-    # schedule breakdown: a fully traced context (events on all three
-    # streams), run back to back like the timed region
-    fctx = make(dlo.FLAG_TRACE)
-    for _ in range(3):
-        fctx.forward(xbuf, cond, T)
-    torch.cuda.synchronize()
-    tr = fctx.trace()
-    st = fctx.stats()
-    fctx.close()
+
+    kernels = {}
     by = {}
-    for r in tr:
-        if not r["kind"].startswith("k_"):
-            by.setdefault(r["kind"], []).append(r)
     for r in ktr:
         if r["kind"].startswith("k_"):
             by.setdefault(r["kind"], []).append(r)
-    dur = lambda rs: sum(r["end"] - r["start"] for r in rs)
-
-    def busy(rs):
-        # length of the union of intervals (the two copy engines overlap)
-        tot, cs, ce = 0.0, None, None
-        for r in sorted(rs, key=lambda r: r["start"]):
-            if ce is None or r["start"] > ce:
-                if ce is not None:
-                    tot += ce - cs
-                cs, ce = r["start"], r["end"]
-            else:
-                ce = max(ce, r["end"])
-        return tot + (ce - cs if ce is not None else 0.0)
-
-    h2d_ms, asm_ms, comp_ms = busy(by.get("h2d", [])), busy(by.get("asm", [])), busy(by.get("compute", []))
-    t_fwd = max(r["end"] for r in tr) - min(r["start"] for r in tr)
-    h2d_bytes = sum(r["bytes"] for r in by.get("h2d", []))
-    asm_read = sum(r["bytes"] for r in by.get("asm", []))
-    overlap_E = max(h2d_ms + asm_ms, comp_ms) / t_fwd
-    hidden = (h2d_ms + comp_ms - t_fwd) / min(h2d_ms, comp_ms)
-    # steady state: the staging of blocks 1..L-1 against the compute of
-    # blocks 0..L-2 (what can overlap once the pipeline is full), inside the
-    # window from the first staging of block 1 to the end of compute(L-2)
-    steady = None
-    if L >= 3:
-        st_rs = [r for r in tr if r["kind"] in ("h2d", "asm") and r["block"] >= 1]
-        cp_rs = [r for r in tr if r["kind"] == "compute" and r["block"] <= L - 2]
-        w0 = min(r["start"] for r in st_rs if r["block"] == 1)
-        w1 = max(r["end"] for r in cp_rs if r["block"] == L - 2)
-        clip = lambda rs: [dict(r, start=max(r["start"], w0), end=min(r["end"], w1)) for r in rs
-                           if r["end"] > w0 and r["start"] < w1]
-        h_s = busy(clip([r for r in st_rs if r["kind"] == "h2d"]))
-        a_s = busy(clip([r for r in st_rs if r["kind"] == "asm"]))
-        c_s = busy(clip(cp_rs))
-        win = w1 - w0
-        steady = {"window_ms": win, "sum_h2d_ms": h_s, "sum_asm_ms": a_s, "sum_compute_ms": c_s,
-                  "E": max(h_s + a_s, c_s) / win, "hidden_frac": (h_s + c_s - win) / min(h_s, c_s)}
-    kernels = {}
     for kind in KERNEL_KINDS:
         rs = by.get(kind, [])
         if not rs:
             continue
-        avg = dur(rs) / len(rs)
         ds = sorted(r["end"] - r["start"] for r in rs)
+        avg = sum(ds) / len(ds)
+        med = ds[len(ds) // 2]
         # work per launch follows each launch's block (widths differ between
         # blocks in the irregular workload); average work / average time
         unit = kernel_work(shapes[0], T)[kind][0]
         work = sum(kernel_work(shapes[r["block"]], T)[kind][1] for r in rs) / len(rs)
-        rate = work / (avg * 1e-3)
-        # the median shows how far a few slow launches pull the average
-        e = {"launches": len(rs), "avg_ms": avg, "median_ms": ds[len(ds) // 2], "max_ms": ds[-1], "total_ms": dur(rs),
+        e = {"launches": len(rs), "avg_ms": avg, "median_ms": med, "max_ms": ds[-1], "total_ms": sum(ds),
              "work_per_launch": work, "desc": KERNEL_DESC[kind]}
         if unit == "flop":
-            e["TFLOPs"] = rate / 1e12
-            e["mfma_frac"] = rate / 1e12 / PEAK_BF16_TFLOPS
+            e["TFLOPs"] = work / (avg * 1e-3) / 1e12
+            e["mfma_frac"] = e["TFLOPs"] / PEAK_BF16_TFLOPS
         else:
-            e["GBps"] = rate / 1e9
-            e["hbm_frac"] = rate / 1e9 / PEAK_HBM_GBPS
+            e["GBps"] = work / (avg * 1e-3) / 1e9
+            e["hbm_frac"] = e["GBps"] / PEAK_HBM_GBPS
         kernels[kind] = e
     gemm_kinds = [k for k in ("k_qk", "k_v", "k_out", "k_fc1", "k_fc2") if k in kernels]
     gemm_flops = sum(kernels[k]["work_per_launch"] * kernels[k]["launches"] for k in gemm_kinds)
@@ -337,41 +382,102 @@ def main():
     gemm_util = gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS if gemm_ms else None
     dom = max(kernels, key=lambda k: kernels[k]["total_ms"])
     unit, work = kernel_work(shapes[0], T)[dom][0], kernels[dom]["work_per_launch"]
-    ach = kernels[dom]["TFLOPs"] if unit == "flop" else kernels[dom]["GBps"]
-    src = os.path.join(ROOT, "layerwise_weight_streaming_dit_amd", "csrc",
-                       "attention.hip" if dom == "k_attn" else ("gemm.hip" if unit == "flop" else "norm.hip"))
-    roofline = {"bound": "mfma" if unit == "flop" else "hbm", "achieved": ach,
-                "peak": PEAK_BF16_TFLOPS if unit == "flop" else PEAK_HBM_GBPS,
-                "unit": "TFLOP/s" if unit == "flop" else "GB/s",
-                "frac": ach / (PEAK_BF16_TFLOPS if unit == "flop" else PEAK_HBM_GBPS),
-                "traffic": traffic_from_profiles(src, dom, wl.name),
+    peak = PEAK_BF16_TFLOPS if unit == "flop" else PEAK_HBM_GBPS
+    scale = 1e12 if unit == "flop" else 1e9
+    ach = work / (kernels[dom]["avg_ms"] * 1e-3) / scale
+    ach_med = work / (kernels[dom]["median_ms"] * 1e-3) / scale
+    roofline = {"bound": "mfma" if unit == "flop" else "hbm", "achieved": ach, "peak": peak,
+                "unit": "TFLOP/s" if unit == "flop" else "GB/s", "frac": ach / peak,
+                "traffic": traffic_from_profiles(dom, wl.name),
                 "kernel": f"{dom}: {KERNEL_DESC[dom]}", "avg_launch_ms": kernels[dom]["avg_ms"],
-                # achieved and frac use the average launch; a single launch
-                # caught in one of the device's occasional multi-millisecond
-                # stalls moves it, the median does not
                 "median_launch_ms": kernels[dom]["median_ms"], "max_launch_ms": kernels[dom]["max_ms"],
+                "frac_by_median": ach_med / peak, "launches": kernels[dom]["launches"],
                 "work_per_launch": work, "work_unit": unit}
 
-    # synchronous schedule (H2D -> wait -> reconstruct -> wait -> compute), same kernels
-    serial = enqueue_untraced_us = None
-    if not args.no_serial:
-        sctx = make(dlo.FLAG_SERIALIZE)
-        sctx.forward(xbuf, cond, T)
-        torch.cuda.synchronize()
-        n_s = max(2, args.steps // 4)
-        ts = time.perf_counter()
-        enq_s = 0.0
-        for _ in range(n_s):
-            te = time.perf_counter()
-            sctx.forward(xbuf, cond, T)
-            enq_s += time.perf_counter() - te
-        torch.cuda.synchronize()
-        serial = 1e3 * (time.perf_counter() - ts) / n_s
-        enqueue_untraced_us = 1e6 * enq_s / n_s
-        sctx.close()
+    # ---- untraced pass: host dispatch per step and the untraced step time
+    ctx.set_flags(0)
+    torch.cuda.synchronize()
+    enq, enq_cpu, n_u = 0.0, 0.0, 2
+    tu = time.perf_counter()
+    for _ in range(n_u):
+        te, tc = time.perf_counter(), time.thread_time()
+        step()
+        enq += time.perf_counter() - te
+        enq_cpu += time.thread_time() - tc
+    torch.cuda.synchronize()
+    untraced_ms = 1e3 * (time.perf_counter() - tu) / n_u
+    dispatch_ms = 1e3 * enq / n_u
+    dispatch_cpu_ms = 1e3 * enq_cpu / n_u
+    log(f"untraced: {untraced_ms:.3f} ms/step, host dispatch {dispatch_ms:.3f} ms/step "
+        f"({dispatch_cpu_ms:.3f} ms of thread CPU time)")
 
-    # pinned H2D ceiling with a plain copy of the same size as one block's shards
-    nbytes = 2 * dp * (-(-numels[0] // dp))
+    # one step on an idle device (no previous step to overlap its pipeline
+    # fill with): the difference to the back-to-back step time is what
+    # streaming across step boundaries hides
+    torch.cuda.synchronize()
+    ti = time.perf_counter()
+    step()
+    torch.cuda.synchronize()
+    iso_ms = 1e3 * (time.perf_counter() - ti)
+
+    sched = residency = costs = None
+    serial = None
+    if not args.timed_only:
+        # ---- fully traced pass over two consecutive forwards
+        ctx.set_flags(dlo.FLAG_TRACE | dlo.FLAG_TRACE_SPAN)
+        ctx.reserve_trace(2)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            ctx.forward(xbuf, cond, T)
+        torch.cuda.synchronize()
+        st = ctx.stats()
+        tr = ctx.trace()
+        fwds = sorted({r["forward"] for r in tr})
+        f0, f1 = fwds[0], fwds[-1]
+        Lc = len(ctx.shapes)
+        per_fwd = {f: overlap_of([r for r in tr if r["forward"] == f]) for f in (f0, f1)}
+        h2d_rs = [r for r in tr if r["kind"] == "h2d"]
+        asm_rs = [r for r in tr if r["kind"] == "asm"]
+        h2d_busy, asm_busy = busy(h2d_rs), busy(asm_rs)
+        sched = {"first_forward": per_fwd[f0], "following_forward": per_fwd[f1],
+                 "h2d_GBps_busy": sum(r["bytes"] for r in h2d_rs) / (h2d_busy * 1e-3) / 1e9,
+                 "assemble_GBps": 2 * sum(r["bytes"] for r in asm_rs) / (asm_busy * 1e-3) / 1e9,
+                 "assemble_bytes_note": "reconstruction reads and writes each valid byte once"}
+        costs = step_costs(tr, Lc, f1)
+        costs.update({"host_dispatch_ms_per_step_untraced": dispatch_ms,
+                      "host_dispatch_cpu_ms_per_step_untraced": dispatch_cpu_ms,
+                      "host_dispatch_note": "wall and thread-CPU time of enqueuing one step (wall time includes "
+                                            "waits for space in the device queues); all of it behind the GPU",
+                      "pages_all_gather_overhead_ms_per_step": PAGES_STEP_OVERHEAD_MS})
+        residency = {"slot_high_water_blocks": st["residency_high_water"],
+                     "blocks_on_device_high_water": st["blocks_on_device_high_water"],
+                     "weight_bytes_peak_in_use": st["weight_bytes_peak"],
+                     "weight_bytes_allocated": st["weight_bytes_allocated"],
+                     "max_block_bytes": st["max_block_bytes"],
+                     "allocated_over_max_block": st["weight_bytes_allocated"] / st["max_block_bytes"],
+                     "slot_bytes": st["slot_bytes"], "landing_bytes": st["landing_bytes"],
+                     "landing_chunk_elems": st["landing_chunk_elems"], "workspace_bytes": st["workspace_bytes"],
+                     "note": "from the traced pass over two consecutive forwards: a block counts on the device "
+                             "from its first H2D start (landing buffers included) to its compute end"}
+        log(f"traced pass: step {costs['step_ms']:.2f} ms, E {per_fwd[f1]['E']:.3f}, "
+            f"hidden {per_fwd[f1]['hidden_frac']:.3f}, blocks on device <= {st['blocks_on_device_high_water']}")
+
+        # ---- synchronous schedule (H2D -> wait -> reconstruct -> wait ->
+        # compute), same kernels
+        if not args.no_serial:
+            ctx.set_flags(dlo.FLAG_SERIALIZE)
+            torch.cuda.synchronize()
+            tss = time.perf_counter()
+            step()
+            torch.cuda.synchronize()
+            serial = 1e3 * (time.perf_counter() - tss)
+            log(f"serialized: {serial:.2f} ms/step")
+    st_all = ctx.stats()
+    ctx.close()
+
+    # pinned H2D ceiling: a plain back-to-back copy of (up to 512 MB of) one
+    # block's bytes
+    nbytes = min(2 * dp * (-(-numels[0] // dp)), 512 << 20)
     hsrc = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
     ddst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     side = torch.cuda.Stream()
@@ -385,14 +491,15 @@ def main():
         e1.record(side)
     torch.cuda.synchronize()
     h2d_ceiling = 8 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del W
+    del hsrc, ddst
 
     cpu = None
     if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
-        cpu = cpu_baseline(wl, dp, T, args.cpu_seconds)
+        cpu = cpu_baseline(wl, shapes, T, W_keep, args.cpu_seconds, args.cpu_min_blocks)
 
     value = L * args.steps / elapsed
     shp = shapes[0]
+    h2d_per_step = st_all["h2d_bytes_per_forward"] * repeats
     out = {
         "metric": "streamed DiT blocks/s & tokens/s; H2D GB/s, GEMM MFMA util, overlap %",
         "value": value,
@@ -409,38 +516,31 @@ def main():
                      "fp16 matrix-core operands; fp32 accumulation, softmax, residual and modulation",
         "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) activations)",
         "config": {"workload": wl.description + (f"; first {L} of {wl.num_blocks} blocks streamed"
-                                                 if L < wl.num_blocks else ""), "blocks": L, "d_model": shp.d_model, "heads": shp.n_heads,
+                                                 if L < wl.num_blocks else "") + note,
+                   "blocks": L, "d_model": shp.d_model, "heads": shp.n_heads,
                    "d_mlp": shp.d_mlp, "d_cond": shp.d_cond, "tokens": T, "batch": 1, "dp_size": dp,
-                   "slots": 2, "parallelism": "single GPU"},
+                   "slots": 2, "pinned_host_bytes": pinned_bytes, "parallelism": "single GPU"},
         "tokens_per_s": T * args.steps / elapsed,
         "token_blocks_per_s": T * L * args.steps / elapsed,
-        "h2d_GBps_busy": h2d_bytes / (h2d_ms * 1e-3) / 1e9 if h2d_ms else None,
-        "h2d_GBps_effective": st["h2d_bytes_per_forward"] * args.steps / elapsed / 1e9,
+        "h2d_GBps_effective": h2d_per_step * args.steps / elapsed / 1e9,
+        "h2d_GBps_busy": sched["h2d_GBps_busy"] if sched else None,
         "h2d_ceiling_GBps": h2d_ceiling,
-        "h2d_frac_of_pcie5_x16": (h2d_bytes / (h2d_ms * 1e-3) / 1e9) / PCIE5_X16_GBPS if h2d_ms else None,
-        "assemble_GBps": (asm_read * 2) / (asm_ms * 1e-3) / 1e9 if asm_ms else None,
+        "h2d_frac_of_pcie5_x16": (sched["h2d_GBps_busy"] / PCIE5_X16_GBPS) if sched else None,
+        "assemble_GBps": sched["assemble_GBps"] if sched else None,
         "gemm_mfma_util": gemm_util,
-        "step_boundary": {"isolated_forward_ms": iso_ms, "back_to_back_ms_per_step": ms_per_step,
-                          "host_enqueue_us_per_forward": 1e6 * enqueue_s / args.steps,
-                          "host_enqueue_us_per_block": 1e6 * enqueue_s / args.steps / L,
-                          "host_enqueue_note": "timed context records HIP events around every kernel",
-                          "host_enqueue_us_per_forward_untraced": enqueue_untraced_us},
-        "overlap": {"E": overlap_E, "hidden_frac": hidden, "t_forward_ms": t_fwd, "sum_h2d_ms": h2d_ms,
-                    "sum_asm_ms": asm_ms, "sum_compute_ms": comp_ms, "serialized_ms": serial,
-                    "steady_state": steady},
-        "residency": {"high_water_blocks": st["residency_high_water"],
-                      "high_water_note": "most blocks whose slot was occupied at one instant (from the block's first "
-                                         "reconstruction write to the end of its compute); 1 when each block "
-                                         "travels as one transfer that lands only after the previous block computed",
-                      "slot_bytes": st["slot_bytes"],
-                      "landing_bytes": st["landing_bytes"], "workspace_bytes": st["workspace_bytes"]},
+        "step_boundary": {"isolated_step_ms": iso_ms, "back_to_back_ms_per_step": ms_per_step,
+                          "untraced_back_to_back_ms_per_step": untraced_ms},
+        "step_overhead": costs,
+        "overlap": dict(sched or {}, serialized_ms_per_step=serial),
+        "residency": residency,
         "kernels": kernels,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "setup_s": load_s,
         "gpu": torch.cuda.get_device_name(0),
         "host": host_info(),
     }
-    print(json.dumps(out))
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -69,7 +69,7 @@ extern "C" {
 #endif
 
 #define DLO_API __attribute__((visibility("default")))
-#define DLO_ABI_VERSION 1
+#define DLO_ABI_VERSION 2
 
 typedef int32_t dlo_status;
 #define DLO_OK 0
@@ -98,6 +98,12 @@ typedef int32_t dlo_status;
                                        dlo_get_trace hands them out (at most
                                        2^19 per context; later ones are not
                                        recorded until then) */
+#define DLO_FLAG_TRACE_SPAN 0x10u  /* with DLO_FLAG_TRACE: keep the intervals of
+                                      consecutive forwards (each tagged with
+                                      its forward index) until dlo_get_trace
+                                      hands them out, so one trace shows how
+                                      one forward's last block and the next
+                                      forward's first block overlap */
 
 typedef struct dlo_ctx dlo_ctx;
 
@@ -123,7 +129,10 @@ typedef struct dlo_config {
   int32_t max_tokens;          /* largest token count dlo_forward accepts, in [1, 2^20], and
                                   max_tokens * max(d_model, d_mlp) * 2 bytes below 4 GiB */
   int64_t landing_chunk_elems; /* largest H2D chunk in elements; 0 = default
-                                  min(dp * max shard size, 2^26); else >= 4096.
+                                  min(S_max, ceil(dp * S_max / 4), 2^24) with
+                                  S_max the largest shard (the two landing
+                                  buffers then hold at most half of the
+                                  largest block); else >= 4096.
                                   A block's padded weight is split into equal
                                   chunks of at most this size (they may span
                                   shards, which sit back to back in one pinned
@@ -172,7 +181,7 @@ typedef struct dlo_interval {
   int32_t chunk;     /* chunk index within the block, -1 otherwise */
   int32_t slot;      /* slot written (ASM) or read (COMPUTE), -1 for H2D */
   int32_t landing;   /* landing buffer written (H2D) or read (ASM), -1 otherwise */
-  int32_t reserved;
+  int32_t forward;   /* index of the dlo_forward call (0 = the context's first) */
   int64_t bytes;     /* bytes moved (H2D, ASM reads) or 0 */
   double start_ms;   /* relative to the start of the forward */
   double end_ms;
@@ -186,63 +195,120 @@ typedef struct dlo_stats {
   size_t slot_bytes;           /* bytes of ONE slot = 2 * dp * S_max */
   size_t landing_bytes;        /* both landing buffers */
   size_t workspace_bytes;      /* activations and scratch */
-  int32_t residency_high_water;/* most blocks resident in slots at once, from
-                                  the last traced forward (0 if untraced) */
-  int32_t n_intervals;         /* intervals recorded by the last traced forward */
+  int32_t residency_high_water;/* most blocks in the two slots at once (a block
+                                  holds its slot from its first reconstruction
+                                  start to its compute end), from the traced
+                                  intervals (0 if untraced) */
+  int32_t n_intervals;         /* intervals the statistics below cover */
   double last_forward_ms;      /* first H2D start to last compute end (traced) */
   double sum_h2d_ms;           /* busy time (union of intervals) per kind (traced) */
   double sum_asm_ms;
   double sum_compute_ms;
   int64_t h2d_bytes_per_forward;
+  /* -- device weight memory (release page, TL;DR and section "Double-buffered
+   *    prefetch": two layers' weights on the device at any time) */
+  int64_t landing_chunk_elems; /* H2D chunk size in use (elements) */
+  size_t max_block_bytes;      /* largest padded block, 2 * dp * S_max bytes */
+  size_t weight_bytes_allocated;/* slots + landing buffers: every device byte
+                                  that ever holds weight data */
+  int32_t blocks_on_device_high_water; /* most blocks with any weight bytes on
+                                  the device at once (a block counts from its
+                                  first H2D start, landing buffers included, to
+                                  its compute end), traced; 0 if untraced */
+  int32_t reserved2;
+  int64_t weight_bytes_peak;   /* most weight bytes in use at once (blocks in
+                                  slots at their padded size plus chunks in
+                                  landing buffers), traced; 0 if untraced */
 } dlo_stats;
 
 /* Pure host query: the parameter table, element count and shard size of one
- * block at dp_size.  out may be NULL (then only counts are returned); cap is
- * its capacity.  No device or context needed. */
+ * block at dp_size (release page, section "Weight sharding with AllGather
+ * reconstruction": one flat buffer per layer, cut into dp_size shards of
+ * ceil(numel / dp_size) elements).  out may be NULL (then only counts are
+ * returned); cap is its capacity.  No device or context needed.  Errors:
+ * DLO_E_INVAL for a block shape the kernels cannot run or cap too small. */
 DLO_API dlo_status dlo_block_layout(const dlo_block_desc* block, int32_t dp_size,
                                     int64_t* numel, int64_t* shard_size,
                                     int32_t* n_params, dlo_param_desc* out, int32_t cap);
 
 /* Pure host query, before dlo_create: device bytes the arena must hold.
- * slots = 2 * slot bytes (the two-slot weight residency); landing = the two
- * landing buffers for H2D chunks; workspace = activations for max_tokens;
- * total = the sum plus alignment.  Any output pointer may be NULL. */
+ * slots = 2 * slot bytes (the two buffers "sized to the largest block" of the
+ * release page's section "Double-buffered prefetch with H2D + AllGather
+ * overlap"); landing = the two landing buffers for H2D chunks (the per-rank
+ * receive buffers of the all-gather); workspace = activations for
+ * max_tokens; total = the sum plus alignment.  Any output pointer may be
+ * NULL.  Errors: those of dlo_create's validation. */
 DLO_API dlo_status dlo_required_bytes(const dlo_config* cfg, size_t* slots, size_t* landing,
                                       size_t* workspace, size_t* total);
 
-/* Validate cfg, compute every block's layout and shard size, carve the
- * caller's arena into slots, landing buffers and workspace, create events
- * (and streams if not given).  Allocates no device memory.  *out is owned by
- * the library until dlo_destroy. */
+/* Enable layerwise offload for one model (release page, section "Quick
+ * start": the feature is switched on per model with a dp_size; section
+ * "Double-buffered prefetch": the two slots are allocated once, sized to the
+ * largest block, and shared by every layer).  Validates cfg, computes every
+ * block's layout and shard size, carves the caller's arena into slots,
+ * landing buffers and workspace, and creates events (and streams if not
+ * given).  Allocates no device memory: the arena stays the caller's and must
+ * outlive the context.  *out is owned by the library until dlo_destroy.
+ * Errors: DLO_E_INVAL (bad field, arena NULL or misaligned), DLO_E_DEV_OOM
+ * (arena smaller than dlo_required_bytes' total), DLO_E_HIP (stream or event
+ * creation failed; nothing is left allocated). */
 DLO_API dlo_status dlo_create(const dlo_config* cfg, dlo_ctx** out);
 
-/* Shard and pin one block: numel must equal the block's layout numel
- * (else DLO_E_SHAPE).  Allocates dp_size pinned host shards of
- * S = ceil(numel / dp_size) elements (back to back in one pinned region:
- * shard r at element r * S), copies the flat weight's slice into each and
- * zero-pads the tail.  Keeps no reference to flat_bf16: the caller may free it
- * on return.  Reloading a block replaces its shards; waits for in-flight work
- * on the context's streams first. */
+/* Shard and pin one block (release page, section "Weight sharding with
+ * AllGather reconstruction": each layer's flattened weight is padded to a
+ * multiple of dp_size, cut into equal shards kept in pinned host memory, and
+ * the source parameter is replaced by an empty placeholder).  numel must
+ * equal the block's layout numel (else DLO_E_SHAPE).  Allocates dp_size
+ * pinned host shards of S = ceil(numel / dp_size) elements (back to back in
+ * one pinned region: shard r at element r * S), copies the flat weight's
+ * slice into each and zero-pads the tail.  Keeps no reference to flat_bf16:
+ * the caller may free it on return (the placeholder step).  Reloading a
+ * block replaces its shards; waits for in-flight copies on the context's
+ * streams first.  Errors: DLO_E_INVAL (block index, NULL), DLO_E_SHAPE,
+ * DLO_E_HOST_OOM (pinned allocation failed; the block stays unloaded). */
 DLO_API dlo_status dlo_load_shards(dlo_ctx* ctx, int32_t block, const uint16_t* flat_bf16,
                                    int64_t numel);
 
-/* The streamed forward over every block, in order.  x: device fp32
+/* The streamed forward over every block, in order (release page, section
+ * "Double-buffered prefetch with H2D + AllGather overlap": layer N+1 is copied
+ * host-to-device and gathered on side streams while layer N computes from the
+ * other buffer; compute waits on an event before it switches buffers; the
+ * layer's parameters are re-pointed at slices of its buffer).  x: device fp32
  * [tokens][d of block 0] in, [tokens][d of the last block] out, in place;
  * its buffer must hold tokens * max_d floats.  cond: device fp32 [d_cond].
  * Enqueues on stream (the compute stream) and the context's side streams and
- * returns without waiting; the result is ready when stream reaches it.
+ * returns without waiting; the result is ready when stream reaches it.  The
+ * call's work is ordered after the previous call's on this context even when
+ * the two calls pass different streams (the context's workspace is shared).
  * Consecutive blocks alternate slots, and the alternation continues across
  * calls (block 0 of a call takes the slot the previous call's last block
  * does not use), so back-to-back calls -- one per denoising step -- stream
  * the next call's first block while the previous call's last block computes.
- * Errors before any enqueue: DLO_E_STATE if a block has no shards,
- * DLO_E_INVAL if tokens is outside [1, max_tokens] or a pointer is NULL. */
+ * The copy of a block starts only after the block two places earlier has
+ * finished computing, so at most two blocks' weights are on the device at
+ * any time.  Errors before any enqueue: DLO_E_STATE if a block has no
+ * shards, DLO_E_INVAL if tokens is outside [1, max_tokens] or a pointer is
+ * NULL or misaligned; DLO_E_HIP (context poisoned) if an enqueue fails. */
 DLO_API dlo_status dlo_forward(dlo_ctx* ctx, float* x, const float* cond, int32_t tokens,
                                hipStream_t stream);
 
-/* Synchronise the context's streams, free pinned shards, events and owned
- * streams.  The arena returns to the caller.  NULL is a no-op. */
+/* Tear the context down (release page, section "Double-buffered prefetch":
+ * the buffers live as long as the model).  Synchronises the context's
+ * streams, frees pinned shards, events and owned streams.  The arena returns
+ * to the caller.  NULL is a no-op.  Always returns DLO_OK. */
 DLO_API dlo_status dlo_destroy(dlo_ctx* ctx);
+
+/* Change the context's flags (DLO_FLAG_*) for the forwards enqueued after
+ * this call, so that one pinned shard store serves timed, traced and
+ * serialized runs.  Drops recorded intervals.  Errors: DLO_E_INVAL for an
+ * unknown flag, DLO_E_POISONED. */
+DLO_API dlo_status dlo_set_flags(dlo_ctx* ctx, uint32_t flags);
+
+/* Create, ahead of time, the timing events that `forwards` traced forwards
+ * under the current flags need, so that no event is created while they are
+ * enqueued (creating events mid-run perturbs the timings).  Errors:
+ * DLO_E_INVAL (forwards < 0), DLO_E_HIP. */
+DLO_API dlo_status dlo_reserve_trace(dlo_ctx* ctx, int32_t forwards);
 
 /* The parameter table of block `block` (see dlo_block_layout). */
 DLO_API dlo_status dlo_layout(dlo_ctx* ctx, int32_t block, int64_t* numel, int64_t* shard_size,
@@ -258,16 +324,18 @@ DLO_API dlo_status dlo_get_shard(dlo_ctx* ctx, int32_t block, int32_t rank,
 DLO_API dlo_status dlo_debug_assemble(dlo_ctx* ctx, int32_t block, uint16_t* host_out,
                                       int64_t cap);
 
-/* Counters and the summary of the last traced forward.  Synchronises the
- * context's streams. */
+/* Counters and the summary of the recorded intervals (the last traced
+ * forward, or every forward recorded since the trace was last handed out
+ * under DLO_FLAG_TRACE_SPAN).  Synchronises the context's streams. */
 DLO_API dlo_status dlo_get_stats(dlo_ctx* ctx, dlo_stats* out);
 
-/* The intervals of the last traced forward (DLO_FLAG_TRACE) or, with
- * DLO_FLAG_TRACE_KERNELS alone, of every forward since the previous call that
- * returned intervals (those are then cleared); cap entries at most, *n
- * receives the number recorded (call with out = NULL to size the buffer; that
- * clears nothing).  Times are in ms from the earliest recorded event.
- * Synchronises the context's streams. */
+/* The recorded intervals: those of the last traced forward (DLO_FLAG_TRACE),
+ * or of every forward since the previous call that returned intervals
+ * (DLO_FLAG_TRACE with DLO_FLAG_TRACE_SPAN, or DLO_FLAG_TRACE_KERNELS alone;
+ * those are then cleared); cap entries at most, *n receives the number
+ * recorded (call with out = NULL to size the buffer; that clears nothing).
+ * Times are in ms from the earliest recorded event.  Synchronises the
+ * context's streams. */
 DLO_API dlo_status dlo_get_trace(dlo_ctx* ctx, dlo_interval* out, int32_t cap, int32_t* n);
 
 /* Message of the last failed call on this thread ("" if none). */

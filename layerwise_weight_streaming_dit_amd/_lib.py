@@ -17,11 +17,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdlo.so")
 HEADERS = [os.path.join(os.path.dirname(_HERE), "include", h) for h in ("dlo.h", "dlo_ops.h")]
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 OK, E_INVAL, E_SHAPE, E_STATE, E_HOST_OOM, E_DEV_OOM, E_HIP, E_POISONED = 0, -1, -2, -3, -4, -5, -6, -7
 STATUS_NAMES = {0: "DLO_OK", -1: "DLO_E_INVAL", -2: "DLO_E_SHAPE", -3: "DLO_E_STATE", -4: "DLO_E_HOST_OOM",
                 -5: "DLO_E_DEV_OOM", -6: "DLO_E_HIP", -7: "DLO_E_POISONED"}
-FLAG_TRACE, FLAG_SERIALIZE, FLAG_POISON_SLOTS, FLAG_TRACE_KERNELS = 0x1, 0x2, 0x4, 0x8
+FLAG_TRACE, FLAG_SERIALIZE, FLAG_POISON_SLOTS, FLAG_TRACE_KERNELS, FLAG_TRACE_SPAN = 0x1, 0x2, 0x4, 0x8, 0x10
 IV_H2D, IV_ASM, IV_COMPUTE = 0, 1, 2
 IV_NAMES = {0: "h2d", 1: "asm", 2: "compute", 3: "k_adaln", 4: "k_ln1", 5: "k_qk", 6: "k_v", 7: "k_attn",
             8: "k_out", 9: "k_ln2", 10: "k_fc1", 11: "k_fc2"}
@@ -56,7 +56,7 @@ class ParamDesc(ctypes.Structure):
 
 class Interval(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("block", ctypes.c_int32), ("chunk", ctypes.c_int32),
-                ("slot", ctypes.c_int32), ("landing", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("slot", ctypes.c_int32), ("landing", ctypes.c_int32), ("forward", ctypes.c_int32),
                 ("bytes", ctypes.c_int64), ("start_ms", ctypes.c_double), ("end_ms", ctypes.c_double)]
 
 
@@ -67,7 +67,10 @@ class Stats(ctypes.Structure):
                 ("residency_high_water", ctypes.c_int32), ("n_intervals", ctypes.c_int32),
                 ("last_forward_ms", ctypes.c_double), ("sum_h2d_ms", ctypes.c_double),
                 ("sum_asm_ms", ctypes.c_double), ("sum_compute_ms", ctypes.c_double),
-                ("h2d_bytes_per_forward", ctypes.c_int64)]
+                ("h2d_bytes_per_forward", ctypes.c_int64), ("landing_chunk_elems", ctypes.c_int64),
+                ("max_block_bytes", ctypes.c_size_t), ("weight_bytes_allocated", ctypes.c_size_t),
+                ("blocks_on_device_high_water", ctypes.c_int32), ("reserved2", ctypes.c_int32),
+                ("weight_bytes_peak", ctypes.c_int64)]
 
 
 _P = ctypes.c_void_p
@@ -81,6 +84,8 @@ _SIGNATURES = {
     "dlo_load_shards": [_P, _I32, _P, _I64],
     "dlo_forward": [_P, _P, _P, _I32, _P],
     "dlo_destroy": [_P],
+    "dlo_set_flags": [_P, ctypes.c_uint32],
+    "dlo_reserve_trace": [_P, _I32],
     "dlo_layout": [_P, _I32, ctypes.POINTER(_I64), ctypes.POINTER(_I64), ctypes.POINTER(_I32),
                    ctypes.POINTER(ParamDesc), _I32],
     "dlo_get_shard": [_P, _I32, _I32, ctypes.POINTER(_P), ctypes.POINTER(_I64)],
@@ -247,6 +252,17 @@ class StreamedDiT:
         check(lib().dlo_debug_assemble(self._h, block, out.ctypes.data, numel))
         return out
 
+    def set_flags(self, flags: int) -> None:
+        """New DLO_FLAG_* for the forwards enqueued from now on (drops any
+        recorded intervals)."""
+        check(lib().dlo_set_flags(self._h, flags))
+        self.flags = flags
+
+    def reserve_trace(self, forwards: int) -> None:
+        """Create the timing events `forwards` traced forwards need now, so
+        none is created while they are enqueued."""
+        check(lib().dlo_reserve_trace(self._h, forwards))
+
     def stats(self) -> Dict:
         s = Stats()
         check(lib().dlo_get_stats(self._h, ctypes.byref(s)))
@@ -258,7 +274,8 @@ class StreamedDiT:
         arr = (Interval * max(1, n.value))()
         check(lib().dlo_get_trace(self._h, arr, n.value, ctypes.byref(n)))
         return [dict(kind=IV_NAMES[iv.kind], block=iv.block, chunk=iv.chunk, slot=iv.slot, landing=iv.landing,
-                     bytes=iv.bytes, start=iv.start_ms, end=iv.end_ms) for iv in arr[: n.value]]
+                     forward=iv.forward, bytes=iv.bytes, start=iv.start_ms, end=iv.end_ms)
+                for iv in arr[: n.value]]
 
     def close(self) -> None:
         if getattr(self, "_h", None):

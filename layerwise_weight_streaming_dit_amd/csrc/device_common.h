@@ -30,9 +30,11 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 }
 
 // Eight bf16 weights -> eight fp16 operands for the fp16 matrix cores.  A bf16
-// value has 8 significant bits and fp16 has 11, so the widening is exact for
-// every weight of magnitude >= 2^-14; smaller ones become fp16 subnormals
-// (absolute error <= 2^-25).
+// value has 8 significant bits and fp16 has 11.  Magnitudes in [2^-14, 65504]
+// are fp16 normals and widen exactly; in [2^-17, 2^-14) they become fp16
+// subnormals (spacing 2^-24), which still hold all 8 bits of a bf16 value
+// there, so they widen exactly too; below 2^-17 they round to the subnormal
+// grid (absolute error <= 2^-25); above 65504 they overflow.
 __device__ __forceinline__ f16x8_t bf16x8_to_f16x8(bf16x8_t v) {
   const u32x4_t w = __builtin_bit_cast(u32x4_t, v);
   u32x4_t o;

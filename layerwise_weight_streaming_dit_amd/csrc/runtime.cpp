@@ -22,7 +22,9 @@
 //
 // Per block b (slot k = (b + parity) % 2) the host enqueues, without ever
 // blocking:
-//   copy stream j%2: per chunk j: wait land_free[j%2]; H2D -> landing[j%2];
+//   copy stream j%2: per chunk j: (first two chunks: wait comp_done[k], the
+//                   compute of block b-2, so no third block reaches the
+//                   device); wait land_free[j%2]; H2D -> landing[j%2];
 //                   record h2d_done[j%2]
 //   gather stream : wait comp_done[k] (compute of block b-2 released slot k);
 //                   per chunk j: wait h2d_done[j%2]; reconstruct into slot k;
@@ -52,10 +54,11 @@ namespace dlo {
 namespace {
 
 constexpr size_t kAlign = 256;
-// Default H2D chunk (128 MB): larger transfers run closer to the pinned
-// link's rate (image-shape forward: 55.3 / 54.5 / 53.7 / 53.5 ms with 16 / 32
-// / 64 / 128 MB chunks, against 52.6 ms for back-to-back raw copies).
-constexpr int64_t kDefaultChunk = int64_t(1) << 26;
+// Default H2D chunk: min(largest shard, a quarter of the largest padded block,
+// 2^24 elements = 32 MiB).  The two landing buffers then add at most half a
+// block, and at most 64 MiB, to the two slots' weight bytes: slots + landing
+// <= 2.5 x the largest block at any dp.
+constexpr int64_t kDefaultChunk = int64_t(1) << 24;
 constexpr int64_t kMinChunk = 4096;
 constexpr int kLandSlack = 8;  // landing offset (elements) used to co-align with the slot
 constexpr size_t kMaxTraceEvents = size_t(1) << 20;  // bound on recorded trace events per context
@@ -75,6 +78,28 @@ struct Chunk {
   int64_t valid;  // elements reconstructed (the trailing padding is dropped)
 };
 
+// Cut a block's padded weight (dp * shard elements, of which the first numel
+// are the flat weight) into equal chunks of at most `chunk` elements; lengths
+// are multiples of 8 elements unless `chunk` itself is not.
+std::vector<Chunk> plan_chunks(int dp, int64_t shard, int64_t numel, int64_t chunk) {
+  std::vector<Chunk> out;
+  const int64_t total = int64_t(dp) * shard;
+  const int64_t nch = std::max<int64_t>(1, (total + chunk - 1) / chunk);
+  const int64_t len = std::min(chunk, ((total + nch - 1) / nch + 7) / 8 * 8);
+  for (int64_t off = 0; off < total; off += len) {
+    Chunk c;
+    c.off = off;
+    c.len = std::min(len, total - off);
+    c.valid = std::max<int64_t>(0, std::min(c.len, numel - off));
+    out.push_back(c);
+  }
+  return out;
+}
+
+// Elements a landing buffer needs for a chunk: the chunk lands at the same
+// address modulo 16 bytes as its slot destination.
+int64_t landing_need(const Chunk& c) { return c.off % kLandSlack + c.len; }
+
 struct Block {
   dlo_block_desc desc{};
   std::vector<int64_t> extra;
@@ -86,7 +111,7 @@ struct Block {
 };
 
 struct TraceEv {
-  int kind, block, chunk, slot, landing;
+  int kind, block, chunk, slot, landing, fwd;
   int64_t bytes;
   hipEvent_t start, end;
 };
@@ -100,6 +125,30 @@ struct Workspace {
   uint16_t* u = nullptr;
   float* xalt = nullptr;
 };
+
+// The activation workspace of a forward over T tokens, carved from `base`
+// (256-byte aligned) in a fixed order; returns the bytes it spans.  Every
+// region is written by a kernel before any kernel reads it, so no region
+// needs clearing.
+size_t carve_workspace(char* base, size_t T, size_t d, size_t m, bool mixed, Workspace* w) {
+  const size_t Tp = align_up(T, 64);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* r = base ? base + off : nullptr;
+    off += align_up(bytes, kAlign);
+    return r;
+  };
+  Workspace ws;
+  ws.mod = reinterpret_cast<float*>(take(6 * d * 4));
+  ws.h = reinterpret_cast<uint16_t*>(take(T * d * 2));
+  ws.qk = reinterpret_cast<uint16_t*>(take(T * 2 * d * 2));
+  ws.vt = reinterpret_cast<uint16_t*>(take(d * Tp * 2));
+  ws.o = reinterpret_cast<uint16_t*>(take(T * d * 2));
+  ws.u = reinterpret_cast<uint16_t*>(take(T * m * 2));
+  if (mixed) ws.xalt = reinterpret_cast<float*>(take(T * d * 4));
+  if (w) *w = ws;
+  return off;
+}
 
 }  // namespace
 
@@ -177,6 +226,9 @@ dlo_status validate_config(const dlo_config* cfg) {
   if (cfg->dp_size < 1 || cfg->dp_size > 1024) return fail(DLO_E_INVAL, "dp_size %d outside [1, 1024]", cfg->dp_size);
   if (cfg->max_tokens < 1 || cfg->max_tokens > (1 << 20))
     return fail(DLO_E_INVAL, "max_tokens %d outside [1, 2^20]", cfg->max_tokens);
+  constexpr uint32_t kKnownFlags = DLO_FLAG_TRACE | DLO_FLAG_SERIALIZE | DLO_FLAG_POISON_SLOTS |
+                                   DLO_FLAG_TRACE_KERNELS | DLO_FLAG_TRACE_SPAN;
+  if (cfg->flags & ~kKnownFlags) return fail(DLO_E_INVAL, "unknown flags 0x%x", cfg->flags & ~kKnownFlags);
   if (cfg->landing_chunk_elems != 0 && cfg->landing_chunk_elems < kMinChunk)
     return fail(DLO_E_INVAL, "landing_chunk_elems %lld below %lld", (long long)cfg->landing_chunk_elems,
                 (long long)kMinChunk);
@@ -213,21 +265,22 @@ dlo_status compute_sizes(const dlo_config* cfg, Sizes* z) {
                 cfg->max_tokens);
   // largest padded block, dp * S_max elements: no chunk needs to be longer
   const int64_t padded_max = int64_t(cfg->dp_size) * z->s_max;
-  z->chunk = cfg->landing_chunk_elems ? cfg->landing_chunk_elems : std::min<int64_t>(padded_max, kDefaultChunk);
+  z->chunk = cfg->landing_chunk_elems ? cfg->landing_chunk_elems
+                                      : std::min<int64_t>({z->s_max, ceil_div(padded_max, 4), kDefaultChunk});
+  z->chunk = std::max<int64_t>(z->chunk, std::min<int64_t>(kMinChunk, padded_max));
   z->chunk = std::min<int64_t>(z->chunk, padded_max);
   z->slot_bytes = align_up(size_t(2) * size_t(cfg->dp_size) * size_t(z->s_max), kAlign);
-  z->landing_bytes = 2 * align_up(size_t(2) * size_t(z->chunk + kLandSlack), kAlign);
-  const size_t T = size_t(cfg->max_tokens), Tp = align_up(T, 64);
-  const size_t d = size_t(z->d_max), m = size_t(z->m_max);
-  size_t ws = 0;
-  ws += align_up(6 * d * 4, kAlign);         // mod
-  ws += align_up(T * d * 2, kAlign);         // h
-  ws += align_up(T * 2 * d * 2, kAlign);     // qk
-  ws += align_up(d * Tp * 2, kAlign);        // vt
-  ws += align_up(T * d * 2, kAlign);         // o
-  ws += align_up(T * m * 2, kAlign);         // u
-  if (z->mixed) ws += align_up(T * d * 4, kAlign);  // xalt
-  z->workspace_bytes = ws;
+  // each landing buffer holds the largest chunk any block is cut into
+  int64_t land = 0;
+  for (int i = 0; i < cfg->num_blocks; ++i) {
+    BlockLayout L;
+    (void)compute_layout(&cfg->blocks[i], &L);
+    for (const Chunk& c : plan_chunks(cfg->dp_size, ceil_div(L.numel, cfg->dp_size), L.numel, z->chunk))
+      land = std::max(land, landing_need(c));
+  }
+  z->landing_bytes = 2 * align_up(size_t(2) * size_t(land), kAlign);
+  z->workspace_bytes = carve_workspace(nullptr, size_t(cfg->max_tokens), size_t(z->d_max), size_t(z->m_max),
+                                       z->mixed, nullptr);
   z->total = 2 * z->slot_bytes + z->landing_bytes + z->workspace_bytes;
   return DLO_OK;
 }
@@ -252,19 +305,37 @@ void copy_parallel(void* dst, const void* src, size_t bytes) {
   for (auto& th : pool) th.join();
 }
 
-void build_chunks(Block& b, int dp, int64_t chunk) {
-  b.chunks.clear();
-  const int64_t total = int64_t(dp) * b.shard, n = b.layout.numel;
-  // equal chunks (multiples of 8 elements) of at most `chunk` elements
-  const int64_t nch = std::max<int64_t>(1, (total + chunk - 1) / chunk);
-  const int64_t len = std::min(chunk, ((total + nch - 1) / nch + 7) / 8 * 8);
-  for (int64_t off = 0; off < total; off += len) {
-    Chunk c;
-    c.off = off;
-    c.len = std::min(len, total - off);
-    c.valid = std::max<int64_t>(0, std::min(c.len, n - off));
-    b.chunks.push_back(c);
+// Index of the forward being enqueued (forwards counts completed enqueues).
+int fwd_index(const dlo_ctx* ctx) { return static_cast<int>(ctx->forwards); }
+
+// Trace events one forward records under the context's current flags.
+size_t events_per_forward(const dlo_ctx* ctx) {
+  const bool all = (ctx->flags & DLO_FLAG_TRACE) != 0;
+  const bool kern = all || (ctx->flags & DLO_FLAG_TRACE_KERNELS) != 0;
+  if (!kern) return 0;
+  size_t n = 0;
+  for (auto& b : ctx->blocks) n += 2 + 2 * 9 + (all ? 4 * b.chunks.size() : 0);
+  return n;
+}
+
+// Create pool events until `want` exist (bounded); false if creation failed.
+bool grow_pool(dlo_ctx* ctx, size_t want) {
+  want = std::min(want, kMaxTraceEvents);
+  while (ctx->ev_pool.size() < want) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreateWithFlags(&e, kTraceEventFlags) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    ctx->ev_pool.push_back(e);
   }
+  return true;
+}
+
+void drop_trace(dlo_ctx* ctx) {
+  ctx->trace.clear();
+  ctx->ev_next = 0;
+  ctx->trace_valid = false;
 }
 
 hipEvent_t next_ev(dlo_ctx* ctx) {
@@ -294,7 +365,13 @@ dlo_status enqueue_staging(dlo_ctx* ctx, int b, int k, bool trace, bool in_forwa
     const int64_t co = c.off % kLandSlack;  // co-align landing with slot (mod 16 bytes)
     uint16_t* land = ctx->landing[lb] + co;
     hipStream_t cs = lb ? ctx->copy_s2 : ctx->copy_s;
-    // copy stream of this landing buffer
+    // copy stream of this landing buffer.  The first chunk on each of the two
+    // copy streams waits for the compute of block b-2 (the last reader of
+    // slot k): a block's weights reach the device only once the block two
+    // places earlier is done, so at most two blocks -- the one computing and
+    // the one being staged, landing buffers included -- are ever on the
+    // device.  Later chunks follow on the same streams.
+    if (ci < 2) DLO_HIP(ctx, hipStreamWaitEvent(cs, ctx->comp_done[k], 0));
     DLO_HIP(ctx, hipStreamWaitEvent(cs, ctx->land_free[lb], 0));
     if ((ctx->flags & DLO_FLAG_SERIALIZE) && in_forward) {
       // synchronous schedule: nothing of block b moves before block b-1 computed
@@ -302,7 +379,7 @@ dlo_status enqueue_staging(dlo_ctx* ctx, int b, int k, bool trace, bool in_forwa
     }
     TraceEv tv{};
     if (trace) {
-      tv = TraceEv{DLO_IV_H2D, b, static_cast<int>(ci), -1, lb, c.len * 2, next_ev(ctx), next_ev(ctx)};
+      tv = TraceEv{DLO_IV_H2D, b, static_cast<int>(ci), -1, lb, fwd_index(ctx), c.len * 2, next_ev(ctx), next_ev(ctx)};
       if (tv.start) DLO_HIP(ctx, hipEventRecord(tv.start, cs));
     }
     DLO_HIP(ctx, hipMemcpyAsync(land, blk.pinned + c.off, size_t(c.len) * 2, hipMemcpyHostToDevice, cs));
@@ -320,7 +397,7 @@ dlo_status enqueue_staging(dlo_ctx* ctx, int b, int k, bool trace, bool in_forwa
     DLO_HIP(ctx, hipStreamWaitEvent(ctx->gather_s, ctx->h2d_done[lb], 0));
     TraceEv ta{};
     if (trace) {
-      ta = TraceEv{DLO_IV_ASM, b, static_cast<int>(ci), k, lb, c.valid * 2, next_ev(ctx), next_ev(ctx)};
+      ta = TraceEv{DLO_IV_ASM, b, static_cast<int>(ci), k, lb, fwd_index(ctx), c.valid * 2, next_ev(ctx), next_ev(ctx)};
       if (ta.start) DLO_HIP(ctx, hipEventRecord(ta.start, ctx->gather_s));
     }
     DLO_HIP(ctx, launch_assemble(ctx->slot[k] + c.off, land, c.valid, ctx->gather_s));
@@ -334,9 +411,10 @@ dlo_status enqueue_staging(dlo_ctx* ctx, int b, int k, bool trace, bool in_forwa
   return DLO_OK;
 }
 
-// The DiT block of `b` from slot k on the compute stream.
+// The DiT block of `b` from slot k on the compute stream, with activations in
+// workspace w.
 dlo_status enqueue_block_compute(dlo_ctx* ctx, int b, int k, float*& x_cur, int& d_cur, float* x_user,
-                                 const float* cond, int T, hipStream_t s, bool trace) {
+                                 const float* cond, int T, hipStream_t s, bool trace, const Workspace& w) {
   const Block& blk = ctx->blocks[b];
   const BlockLayout& L = blk.layout;
   const uint16_t* base = ctx->slot[k];
@@ -354,13 +432,12 @@ dlo_status enqueue_block_compute(dlo_ctx* ctx, int b, int k, float*& x_cur, int&
   const int d = blk.desc.d_model, m = blk.desc.d_mlp, H = blk.desc.n_heads, c = blk.desc.d_cond;
   const int hd = d / H;
   const int Tp = static_cast<int>(align_up(size_t(T), 64));
-  const Workspace& w = ctx->ws;
   float* mod = w.mod;
   // Record a timed interval around one kernel when tracing.
   auto timed = [&](int kind, auto&& launch) -> dlo_status {
     TraceEv tv{};
     if (trace) {
-      tv = TraceEv{kind, b, -1, k, -1, 0, next_ev(ctx), next_ev(ctx)};
+      tv = TraceEv{kind, b, -1, k, -1, fwd_index(ctx), 0, next_ev(ctx), next_ev(ctx)};
       if (tv.start) DLO_HIP(ctx, hipEventRecord(tv.start, s));
     }
     DLO_HIP(ctx, launch());
@@ -491,7 +568,7 @@ extern "C" DLO_API dlo_status dlo_create(const dlo_config* cfg, dlo_ctx** out) {
     st = compute_layout(&b.desc, &b.layout);
     if (st != DLO_OK) return st;
     b.shard = ceil_div(b.layout.numel, ctx->dp);
-    build_chunks(b, ctx->dp, ctx->chunk_elems);
+    b.chunks = plan_chunks(ctx->dp, b.shard, b.layout.numel, ctx->chunk_elems);
   }
   // carve the arena: slot 0, slot 1, landing 0, landing 1, workspace
   char* p = static_cast<char*>(cfg->arena);
@@ -504,19 +581,7 @@ extern "C" DLO_API dlo_status dlo_create(const dlo_config* cfg, dlo_ctx** out) {
   p += land_one;
   ctx->landing[1] = reinterpret_cast<uint16_t*>(p);
   p += land_one;
-  const size_t T = size_t(cfg->max_tokens), Tp = align_up(T, 64), d = size_t(z.d_max), m = size_t(z.m_max);
-  auto take = [&](size_t bytes) {
-    char* r = p;
-    p += align_up(bytes, kAlign);
-    return r;
-  };
-  ctx->ws.mod = reinterpret_cast<float*>(take(6 * d * 4));
-  ctx->ws.h = reinterpret_cast<uint16_t*>(take(T * d * 2));
-  ctx->ws.qk = reinterpret_cast<uint16_t*>(take(T * 2 * d * 2));
-  ctx->ws.vt = reinterpret_cast<uint16_t*>(take(d * Tp * 2));
-  ctx->ws.o = reinterpret_cast<uint16_t*>(take(T * d * 2));
-  ctx->ws.u = reinterpret_cast<uint16_t*>(take(T * m * 2));
-  if (z.mixed) ctx->ws.xalt = reinterpret_cast<float*>(take(T * d * 4));
+  carve_workspace(p, size_t(cfg->max_tokens), size_t(z.d_max), size_t(z.m_max), z.mixed, &ctx->ws);
 
   DeviceGuard dg(ctx->device);
   if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
@@ -546,12 +611,7 @@ extern "C" DLO_API dlo_status dlo_create(const dlo_config* cfg, dlo_ctx** out) {
     DLO_HIP(nullptr, hipEventRecord(c->land_free[i], c->gather_s));
     DLO_HIP(nullptr, hipEventRecord(c->comp_done[i], c->gather_s));
   }
-  if (c->flags & (DLO_FLAG_TRACE | DLO_FLAG_TRACE_KERNELS)) {
-    size_t n = 0;
-    for (auto& b : c->blocks) n += 4 * b.chunks.size() + 2 + 2 * 9;
-    c->ev_pool.resize(n, nullptr);
-    for (size_t i = 0; i < n; ++i) DLO_HIP(nullptr, hipEventCreateWithFlags(&c->ev_pool[i], kTraceEventFlags));
-  }
+  if (!grow_pool(c, events_per_forward(c))) return fail(DLO_E_HIP, "trace event creation failed");
   DLO_HIP(nullptr, hipStreamSynchronize(c->gather_s));
   *out = ctx.release();
   return DLO_OK;
@@ -593,9 +653,11 @@ extern "C" DLO_API dlo_status dlo_load_shards(dlo_ctx* ctx, int32_t block, const
   return DLO_OK;
 }
 
-extern "C" DLO_API dlo_status dlo_forward(dlo_ctx* ctx, float* x, const float* cond, int32_t tokens,
-                                          hipStream_t stream) {
-  clear_error();
+namespace dlo {
+namespace {
+
+// Validation shared by the forward entry points (before any enqueue).
+dlo_status check_forward(dlo_ctx* ctx, const float* x, const float* cond, int32_t tokens) {
   dlo_status st = check_ctx(ctx);
   if (st != DLO_OK) return st;
   if (x == nullptr || cond == nullptr) return fail(DLO_E_INVAL, "x or cond is NULL");
@@ -603,23 +665,34 @@ extern "C" DLO_API dlo_status dlo_forward(dlo_ctx* ctx, float* x, const float* c
     return fail(DLO_E_INVAL, "tokens %d outside [1, %d]", tokens, ctx->max_tokens);
   if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(cond) % 16)
     return fail(DLO_E_INVAL, "x and cond must be 16-byte aligned");
+  return DLO_OK;
+}
+
+dlo_status check_loaded(dlo_ctx* ctx) {
   for (size_t i = 0; i < ctx->blocks.size(); ++i)
     if (ctx->blocks[i].shards.empty()) return fail(DLO_E_STATE, "block %zu has no shards loaded", i);
+  return DLO_OK;
+}
+
+// The streamed forward with activations in workspace w (validated).
+dlo_status forward_impl(dlo_ctx* ctx, float* x, const float* cond, int32_t tokens, hipStream_t stream,
+                        const Workspace& w) {
   DeviceGuard dg(ctx->device);
   if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
 
   const bool trace_all = (ctx->flags & DLO_FLAG_TRACE) != 0;
   const bool trace = trace_all || (ctx->flags & DLO_FLAG_TRACE_KERNELS) != 0;
-  if (trace_all) {
-    // the full trace describes the last forward only
-    ctx->trace.clear();
-    ctx->ev_next = 0;
-    ctx->trace_valid = false;
-  }
+  // the full trace describes the last forward only, unless it spans forwards
+  if (trace_all && !(ctx->flags & DLO_FLAG_TRACE_SPAN)) drop_trace(ctx);
   float* x_cur = x;
   int d_cur = ctx->blocks[0].desc.d_model;
   const int L = static_cast<int>(ctx->blocks.size());
   const int parity = ctx->parity;
+  dlo_status st;
+  // The workspace (and x) are shared with the previous call, whose last block
+  // computed from slot parity ^ 1: order this call after it even if the
+  // caller switched streams (free when it is the same stream).
+  DLO_HIP(ctx, hipStreamWaitEvent(stream, ctx->comp_done[parity ^ 1], 0));
   for (int b = 0; b < L; ++b) {
     const int k = (b + parity) & 1;
     st = enqueue_staging(ctx, b, k, trace_all, true);
@@ -627,10 +700,10 @@ extern "C" DLO_API dlo_status dlo_forward(dlo_ctx* ctx, float* x, const float* c
     DLO_HIP(ctx, hipStreamWaitEvent(stream, ctx->asm_done[k], 0));
     TraceEv tc{};
     if (trace) {
-      tc = TraceEv{DLO_IV_COMPUTE, b, -1, k, -1, 0, next_ev(ctx), next_ev(ctx)};
+      tc = TraceEv{DLO_IV_COMPUTE, b, -1, k, -1, fwd_index(ctx), 0, next_ev(ctx), next_ev(ctx)};
       if (tc.start) DLO_HIP(ctx, hipEventRecord(tc.start, stream));
     }
-    st = enqueue_block_compute(ctx, b, k, x_cur, d_cur, x, cond, tokens, stream, trace);
+    st = enqueue_block_compute(ctx, b, k, x_cur, d_cur, x, cond, tokens, stream, trace, w);
     if (st != DLO_OK) return st;
     if (trace && tc.end) {
       DLO_HIP(ctx, hipEventRecord(tc.end, stream));
@@ -644,6 +717,18 @@ extern "C" DLO_API dlo_status dlo_forward(dlo_ctx* ctx, float* x, const float* c
   ctx->parity ^= L & 1;
   ++ctx->forwards;
   return DLO_OK;
+}
+
+}  // namespace
+}  // namespace dlo
+
+extern "C" DLO_API dlo_status dlo_forward(dlo_ctx* ctx, float* x, const float* cond, int32_t tokens,
+                                          hipStream_t stream) {
+  clear_error();
+  dlo_status st = check_forward(ctx, x, cond, tokens);
+  if (st == DLO_OK) st = check_loaded(ctx);
+  if (st != DLO_OK) return st;
+  return forward_impl(ctx, x, cond, tokens, stream, ctx->ws);
 }
 
 extern "C" DLO_API dlo_status dlo_destroy(dlo_ctx* ctx) {
@@ -716,6 +801,20 @@ extern "C" DLO_API dlo_status dlo_debug_assemble(dlo_ctx* ctx, int32_t block, ui
 
 namespace {
 
+// Largest number of [start, end) intervals alive at once, each weighted
+// (ends sort before starts at equal times).
+int64_t max_weighted_overlap(std::vector<std::pair<double, int64_t>>& ev) {
+  std::sort(ev.begin(), ev.end(), [](const auto& u, const auto& v) {
+    return u.first < v.first || (u.first == v.first && u.second < v.second);
+  });
+  int64_t cur = 0, best = 0;
+  for (auto& e : ev) {
+    cur += e.second;
+    best = std::max(best, cur);
+  }
+  return best;
+}
+
 dlo_status collect_trace(dlo_ctx* ctx, std::vector<dlo_interval>& out, dlo_stats* s) {
   out.clear();
   if (!ctx->trace_valid) return DLO_OK;
@@ -748,6 +847,7 @@ dlo_status collect_trace(dlo_ctx* ctx, std::vector<dlo_interval>& out, dlo_stats
     iv.chunk = t.chunk;
     iv.slot = t.slot;
     iv.landing = t.landing;
+    iv.forward = t.fwd;
     iv.bytes = t.bytes;
     iv.start_ms = double(a) - double(best);
     iv.end_ms = double(e) - double(best);
@@ -780,29 +880,71 @@ dlo_status collect_trace(dlo_ctx* ctx, std::vector<dlo_interval>& out, dlo_stats
     s->sum_h2d_ms = h;
     s->sum_asm_ms = a;
     s->sum_compute_ms = c;
-    // residency: block b occupies its slot from its first reconstruction
-    // start to its compute end
-    const int L = static_cast<int>(ctx->blocks.size());
-    std::vector<double> first(L, 1e300), last(L, -1e300);
+    // Residency, per block instance g = forward * L + block:
+    //  * in a slot from its first reconstruction start to its compute end;
+    //  * on the device from its first H2D start (landing buffers included) to
+    //    its compute end;
+    //  * weight bytes: a block in its slot counts its padded size, a chunk in
+    //    a landing buffer counts its length from its H2D start to the end of
+    //    its reconstruction.
+    const int64_t L = static_cast<int64_t>(ctx->blocks.size());
+    struct Span {
+      double asm0 = 1e300, h2d0 = 1e300, comp1 = -1e300;
+    };
+    std::vector<Span> sp;
+    auto at = [&](const dlo_interval& iv) -> Span& {
+      const size_t g = size_t(int64_t(std::max(iv.forward, 0)) * L + iv.block);
+      if (sp.size() <= g) sp.resize(g + 1);
+      return sp[g];
+    };
+    // landing occupancy: chunk (g, j) from its H2D start to its ASM end
+    std::vector<std::pair<double, int64_t>> wev;
+    struct ChunkKey {
+      int64_t g;
+      int chunk;
+      bool operator<(const ChunkKey& o) const { return g < o.g || (g == o.g && chunk < o.chunk); }
+    };
+    std::vector<std::pair<ChunkKey, std::pair<double, int64_t>>> h2d_start;
+    std::vector<std::pair<ChunkKey, double>> asm_end;
     for (auto& iv : out) {
-      if (iv.kind == DLO_IV_ASM) first[iv.block] = std::min(first[iv.block], iv.start_ms);
-      if (iv.kind == DLO_IV_COMPUTE) last[iv.block] = std::max(last[iv.block], iv.end_ms);
+      const int64_t g = int64_t(std::max(iv.forward, 0)) * L + iv.block;
+      if (iv.kind == DLO_IV_ASM) {
+        at(iv).asm0 = std::min(at(iv).asm0, iv.start_ms);
+        asm_end.push_back({ChunkKey{g, iv.chunk}, iv.end_ms});
+      } else if (iv.kind == DLO_IV_H2D) {
+        at(iv).h2d0 = std::min(at(iv).h2d0, iv.start_ms);
+        h2d_start.push_back({ChunkKey{g, iv.chunk}, {iv.start_ms, iv.bytes}});
+      } else if (iv.kind == DLO_IV_COMPUTE) {
+        at(iv).comp1 = std::max(at(iv).comp1, iv.end_ms);
+      }
     }
-    std::vector<std::pair<double, int>> evs;
-    for (int b2 = 0; b2 < L; ++b2) {
-      if (first[b2] > 1e299 || last[b2] < -1e299) continue;  // schedule not traced
-      evs.push_back({first[b2], 1});
-      evs.push_back({last[b2], -1});
+    std::sort(asm_end.begin(), asm_end.end(), [](auto& u, auto& v) { return u.first < v.first; });
+    for (auto& hs : h2d_start) {
+      auto it = std::lower_bound(asm_end.begin(), asm_end.end(), hs.first,
+                                 [](const auto& e, const ChunkKey& k) { return e.first < k; });
+      if (it == asm_end.end() || it->first.g != hs.first.g || it->first.chunk != hs.first.chunk) continue;
+      wev.push_back({hs.second.first, hs.second.second});
+      wev.push_back({it->second, -hs.second.second});
     }
-    std::sort(evs.begin(), evs.end(), [](auto& u, auto& v) {
-      return u.first < v.first || (u.first == v.first && u.second < v.second);
-    });
-    int cur = 0, hw = 0;
-    for (auto& e2 : evs) {
-      cur += e2.second;
-      hw = std::max(hw, cur);
+    std::vector<std::pair<double, int64_t>> slot_ev, dev_ev;
+    for (size_t g = 0; g < sp.size(); ++g) {
+      const Span& q = sp[g];
+      if (q.comp1 < -1e299) continue;  // compute not traced
+      const int64_t bbytes = int64_t(2) * ctx->dp * ctx->blocks[g % size_t(L)].shard;
+      if (q.asm0 < 1e299) {
+        slot_ev.push_back({q.asm0, 1});
+        slot_ev.push_back({q.comp1, -1});
+        wev.push_back({q.asm0, bbytes});
+        wev.push_back({q.comp1, -bbytes});
+      }
+      if (q.h2d0 < 1e299) {
+        dev_ev.push_back({q.h2d0, 1});
+        dev_ev.push_back({q.comp1, -1});
+      }
     }
-    s->residency_high_water = hw;
+    s->residency_high_water = static_cast<int32_t>(max_weighted_overlap(slot_ev));
+    s->blocks_on_device_high_water = static_cast<int32_t>(max_weighted_overlap(dev_ev));
+    s->weight_bytes_peak = max_weighted_overlap(wev);
     s->n_intervals = static_cast<int32_t>(out.size());
   }
   return DLO_OK;
@@ -827,6 +969,9 @@ extern "C" DLO_API dlo_status dlo_get_stats(dlo_ctx* ctx, dlo_stats* out) {
   int64_t hb = 0;
   for (auto& b : ctx->blocks) hb += int64_t(2) * ctx->dp * b.shard;
   out->h2d_bytes_per_forward = hb;
+  out->landing_chunk_elems = ctx->chunk_elems;
+  out->max_block_bytes = size_t(2) * size_t(ctx->dp) * size_t(ctx->s_max);
+  out->weight_bytes_allocated = 2 * ctx->slot_bytes + ctx->landing_bytes;
   std::vector<dlo_interval> tmp;
   return collect_trace(ctx, tmp, out);
 }
@@ -844,12 +989,32 @@ extern "C" DLO_API dlo_status dlo_get_trace(dlo_ctx* ctx, dlo_interval* out, int
   if (out) {
     if (cap < *n) return fail(DLO_E_INVAL, "cap %d < %d intervals", cap, *n);
     memcpy(out, tmp.data(), sizeof(dlo_interval) * tmp.size());
-    if (!(ctx->flags & DLO_FLAG_TRACE)) {
-      // kernel-only tracing: intervals handed out are consumed
-      ctx->trace.clear();
-      ctx->ev_next = 0;
-      ctx->trace_valid = false;
-    }
+    // accumulating traces (kernel-only, or spanning forwards) are consumed
+    if (!(ctx->flags & DLO_FLAG_TRACE) || (ctx->flags & DLO_FLAG_TRACE_SPAN)) drop_trace(ctx);
   }
+  return DLO_OK;
+}
+
+extern "C" DLO_API dlo_status dlo_set_flags(dlo_ctx* ctx, uint32_t flags) {
+  clear_error();
+  dlo_status st = check_ctx(ctx);
+  if (st != DLO_OK) return st;
+  constexpr uint32_t kKnown = DLO_FLAG_TRACE | DLO_FLAG_SERIALIZE | DLO_FLAG_POISON_SLOTS |
+                              DLO_FLAG_TRACE_KERNELS | DLO_FLAG_TRACE_SPAN;
+  if (flags & ~kKnown) return fail(DLO_E_INVAL, "unknown flags 0x%x", flags & ~kKnown);
+  ctx->flags = flags;
+  drop_trace(ctx);
+  return DLO_OK;
+}
+
+extern "C" DLO_API dlo_status dlo_reserve_trace(dlo_ctx* ctx, int32_t forwards) {
+  clear_error();
+  dlo_status st = check_ctx(ctx);
+  if (st != DLO_OK) return st;
+  if (forwards < 0) return fail(DLO_E_INVAL, "forwards %d < 0", forwards);
+  DeviceGuard dg(ctx->device);
+  if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
+  const size_t want = ctx->ev_next + size_t(forwards) * events_per_forward(ctx);
+  if (!grow_pool(ctx, want)) return fail(DLO_E_HIP, "trace event creation failed");
   return DLO_OK;
 }

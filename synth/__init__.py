@@ -37,6 +37,7 @@ __all__ = [
     "bf16_bits_from_f32",
     "block_weights",
     "many_block_weights",
+    "iter_block_weights",
     "activations",
     "conditioning",
     "request_tokens",
@@ -120,12 +121,22 @@ def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
     return ((u + rounding) >> np.uint32(16)).astype(np.uint16)
 
 
+_SLICE = 1 << 24  # draws converted per pass (bounds the fp32 temporaries)
+
+
 def block_weights(wid: int, block: int, numel: int, std: float = 0.02) -> np.ndarray:
-    """The flat bf16 weight of one block as uint16 bit patterns, N(0, std)."""
+    """The flat bf16 weight of one block as uint16 bit patterns, N(0, std).
+    Drawn and rounded slice by slice: the generator's stream continues across
+    calls, so the result is the same as one draw of `numel` values, without
+    a full-size fp32 copy in memory."""
     g = np.random.Generator(np.random.PCG64(weight_seed(wid, block)))
-    a = g.standard_normal(int(numel), dtype=np.float32)
-    a *= np.float32(std)
-    return bf16_bits_from_f32(a)
+    n = int(numel)
+    out = np.empty(n, dtype=np.uint16)
+    for i in range(0, n, _SLICE):
+        a = g.standard_normal(min(_SLICE, n - i), dtype=np.float32)
+        a *= np.float32(std)
+        out[i:i + a.size] = bf16_bits_from_f32(a)
+    return out
 
 
 def many_block_weights(wid: int, numels: Sequence[int], blocks: Optional[Sequence[int]] = None,
@@ -137,6 +148,23 @@ def many_block_weights(wid: int, numels: Sequence[int], blocks: Optional[Sequenc
     blocks = list(blocks)
     with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
         return list(ex.map(lambda bn: block_weights(wid, bn[0], bn[1]), zip(blocks, numels)))
+
+
+def iter_block_weights(wid: int, numels: Sequence[int], threads: int = 8):
+    """Yield (block, flat bf16 weight) in block order, drawing up to `threads`
+    blocks ahead in parallel threads; a block's array is dropped by the caller
+    once consumed, so at most about `threads` blocks are held at once."""
+    from collections import deque
+    numels = list(numels)
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        pending = deque()
+        nxt = 0
+        while nxt < len(numels) or pending:
+            while nxt < len(numels) and len(pending) < max(1, threads):
+                pending.append((nxt, ex.submit(block_weights, wid, nxt, numels[nxt])))
+                nxt += 1
+            b, fut = pending.popleft()
+            yield b, fut.result()
 
 
 def activations(tokens: int, d: int, seed: int = 7) -> np.ndarray:

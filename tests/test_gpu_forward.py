@@ -278,10 +278,122 @@ def test_trace_two_slot_schedule_image():
     numels = [OL.block_numel(s) for s in shapes]
     errs = OT.check_trace(tr, 8, slot_capacity=st["slot_bytes"] // 2, numels=numels, dp=4)
     assert errs == [], errs[:5]
-    assert OT.residency_high_water(tr, 8) <= 2
-    assert st["residency_high_water"] <= 2
     assert st["slot_bytes"] == 2 * OT.slot_capacity_elems(numels, 4)
+    # the library's residency figures are the oracle's, on the same intervals
+    assert st["residency_high_water"] == OT.residency_high_water(tr, 8) <= 2
+    assert st["blocks_on_device_high_water"] == OT.device_high_water(tr, 8) <= 2
+    block_bytes = [2 * 4 * OS.shard_size(n, 4) for n in numels]
+    assert st["weight_bytes_peak"] == OT.weight_bytes_peak(tr, 8, block_bytes)
+    # every device byte that holds weights: two slots and two landing buffers
+    # of one shard each = 2.5 blocks (release page, TL;DR: two layers' weights)
+    assert st["max_block_bytes"] == max(block_bytes)
+    assert st["weight_bytes_allocated"] == 2.5 * st["max_block_bytes"]
+    assert st["weight_bytes_peak"] <= st["weight_bytes_allocated"]
     print("stats", st)
+
+
+def _chain(ctx, x, cond, steps, streams=None, hold_cycles=0):
+    """`steps` back-to-back forwards, each on the previous one's output (a
+    denoising loop), optionally on a different stream per step.  hold_cycles
+    > 0 first parks the compute stream in a bounded spin kernel, so that the
+    host has enqueued every step before the GPU starts on them (the GPU then
+    runs them back to back whatever the host's enqueue speed)."""
+    t = torch()
+    T, d0 = x.shape
+    xbuf = t.zeros(T * ctx.max_d, dtype=t.float32, device="cuda")
+    xbuf[: T * d0] = dev(x.reshape(-1))
+    c = dev(cond)
+    t.cuda.synchronize()
+    if hold_cycles:
+        t.cuda._sleep(hold_cycles)
+    for i in range(steps):
+        out = ctx.forward(xbuf, c, T, stream=None if streams is None else streams[i % len(streams)])
+    t.cuda.synchronize()
+    return host(out).copy()
+
+
+@pytest.mark.parametrize("L", [3, 4])
+def test_next_forward_first_block_streams_under_last_block(L):
+    # A compute-bound shape (d 256, T 16384: attention dominates), cut into
+    # several chunks per block, traced over three back-to-back forwards.
+    shp = synth.BlockShape(256, 4, 1024)
+    T = 16384
+    W = [synth.block_weights(1, b, OL.block_numel(shp)) for b in range(L)]
+    ctx = _ctx([shp] * L, 4, T, flags=dlo.FLAG_TRACE | dlo.FLAG_TRACE_SPAN, chunk=1 << 18)
+    for b in range(L):
+        ctx.load_shards(b, W[b])
+    ctx.reserve_trace(3)
+    x, cond = synth.activations(T, 256), synth.conditioning(256)
+    got = _chain(ctx, x, cond, 3, hold_cycles=100_000_000)
+    tr = ctx.trace()
+    st_numel = OL.block_numel(shp)
+    assert sorted({r["forward"] for r in tr}) == [0, 1, 2]
+    errs = OT.check_trace(tr, L, slot_capacity=4 * OS.shard_size(st_numel, 4), numels=[st_numel] * L, dp=4)
+    assert errs == [], errs[:5]
+    assert OT.device_high_water(tr, L) == 2
+    for s in range(2):
+        last = [r for r in tr if r["kind"] == "compute" and r["forward"] == s and r["block"] == L - 1][0]
+        nxt = [r for r in tr if r["kind"] in ("h2d", "asm") and r["forward"] == s + 1 and r["block"] == 0]
+        assert len({r["chunk"] for r in nxt}) > 1
+        # block 0 of step s+1 is copied and reconstructed while block L-1 of
+        # step s computes, and not before block L-2 of step s released its slot
+        assert max(r["end"] for r in nxt) <= last["end"], (s, max(r["end"] for r in nxt), last)
+        prev = [r for r in tr if r["kind"] == "compute" and r["forward"] == s and r["block"] == L - 2][0]
+        assert min(r["start"] for r in nxt) >= prev["end"]
+    # the same loop untraced on a fresh context gives the same bits
+    ref = _ctx([shp] * L, 4, T, chunk=1 << 18)
+    for b in range(L):
+        ref.load_shards(b, W[b])
+    assert np.array_equal(got, _chain(ref, x, cond, 3))
+
+
+def test_forwards_on_alternating_streams_match_one_stream():
+    # consecutive calls may pass different streams; each call is ordered after
+    # the previous one (the context's workspace and x are shared)
+    t = torch()
+    wl = synth.workload("tiny")
+    W = _weights(wl)
+    ctxs = []
+    for _ in range(2):
+        c = _ctx(list(wl.blocks), 4, wl.tokens)
+        for b, flat in W.items():
+            c.load_shards(b, flat)
+        ctxs.append(c)
+    x, cond = synth.activations(wl.tokens, 256), synth.conditioning(256)
+    one = _chain(ctxs[0], x, cond, 6)
+    two = _chain(ctxs[1], x, cond, 6, streams=[t.cuda.Stream(), t.cuda.Stream()])
+    assert np.array_equal(one, two)
+
+
+def test_set_flags_reuses_one_shard_store():
+    wl = synth.workload("tiny")
+    W = _weights(wl)
+    ctx = _ctx(list(wl.blocks), 4, wl.tokens)
+    for b, flat in W.items():
+        ctx.load_shards(b, flat)
+    x, cond = synth.activations(wl.tokens, 256), synth.conditioning(256)
+    base = _run(ctx, x, cond)
+    assert ctx.trace() == []
+    ctx.set_flags(dlo.FLAG_TRACE)
+    assert np.array_equal(_run(ctx, x, cond), base)
+    tr = ctx.trace()
+    assert {"h2d", "asm", "compute", "k_fc2"} <= {r["kind"] for r in tr}
+    assert OT.check_trace(tr, wl.num_blocks) == []
+    ctx.set_flags(dlo.FLAG_TRACE | dlo.FLAG_SERIALIZE)
+    assert np.array_equal(_run(ctx, x, cond), base)
+    tr = ctx.trace()
+    comp_end = {r["block"]: r["end"] for r in tr if r["kind"] == "compute"}
+    assert all(r["start"] >= comp_end[r["block"] - 1] for r in tr if r["kind"] == "h2d" and r["block"] >= 1)
+    ctx.set_flags(dlo.FLAG_TRACE_KERNELS)
+    ctx.reserve_trace(2)
+    for _ in range(2):
+        assert np.array_equal(_run(ctx, x, cond), base)
+    assert len(ctx.trace()) == 2 * wl.num_blocks * 10
+    ctx.set_flags(0)
+    assert np.array_equal(_run(ctx, x, cond), base)
+    assert ctx.trace() == []
+    with pytest.raises(dlo.DloError):
+        ctx.set_flags(0x400)
 
 
 def test_odd_block_count_alternates_slots_across_forwards():
