@@ -292,6 +292,23 @@ DLO_API dlo_status dlo_load_shards(dlo_ctx* ctx, int32_t block, const uint16_t* 
 DLO_API dlo_status dlo_forward(dlo_ctx* ctx, float* x, const float* cond, int32_t tokens,
                                hipStream_t stream);
 
+/* dlo_forward for callers that cannot allocate device memory at call time
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same schedule, kernels and results as dlo_forward, but the
+ * per-forward activation workspace is the library's own static device
+ * scratch -- 256 MiB per device, held from the first dlo_create on that device
+ * until the process ends -- instead of the arena's workspace region; the
+ * call itself allocates nothing.  Every call on one device shares that
+ * device's scratch: calls whose work may overlap on one device (another
+ * context, another stream without ordering) race and must not be issued.
+ * Nothing in the scratch needs to start cleared: each region is written
+ * before it is read.  Errors before any enqueue: those of dlo_forward, plus
+ * DLO_E_INVAL if `tokens` needs more than 256 MiB of activations, and
+ * DLO_E_STATE if a trace flag is set (tracing creates timing events) or the
+ * scratch could not be mapped on the device. */
+DLO_API dlo_status dlo_forward_static(dlo_ctx* ctx, float* x, const float* cond, int32_t tokens,
+                                      hipStream_t stream);
+
 /* Tear the context down (release page, section "Double-buffered prefetch":
  * the buffers live as long as the model).  Synchronises the context's
  * streams, frees pinned shards, events and owned streams.  The arena returns

@@ -83,6 +83,7 @@ _SIGNATURES = {
     "dlo_create": [ctypes.POINTER(Config), ctypes.POINTER(_P)],
     "dlo_load_shards": [_P, _I32, _P, _I64],
     "dlo_forward": [_P, _P, _P, _I32, _P],
+    "dlo_forward_static": [_P, _P, _P, _I32, _P],
     "dlo_destroy": [_P],
     "dlo_set_flags": [_P, ctypes.c_uint32],
     "dlo_reserve_trace": [_P, _I32],

@@ -36,4 +36,11 @@ hipError_t launch_attention(const uint16_t* qk, int ld_qk, const uint16_t* vt, i
                             uint16_t* o, int ld_o, int tokens, int heads, int head_dim,
                             hipStream_t s);
 
+// The library's static device scratch (scratch.hip): kStaticScratchBytes per
+// device, held from the first call on a device until the process ends.
+// static_scratch returns this device's address of it; `device` must be the
+// current device.
+constexpr size_t kStaticScratchBytes = size_t(256) << 20;
+hipError_t static_scratch(int device, void** out);
+
 }  // namespace dlo

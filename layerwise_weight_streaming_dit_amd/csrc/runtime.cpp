@@ -181,6 +181,8 @@ struct dlo_ctx {
   int64_t forwards = 0;
   bool poisoned = false;
   bool created_events = false;
+  void* static_ws = nullptr;       // this device's address of the library's static scratch
+  hipError_t static_ws_err = hipSuccess;
 };
 
 namespace dlo {
@@ -612,6 +614,10 @@ extern "C" DLO_API dlo_status dlo_create(const dlo_config* cfg, dlo_ctx** out) {
     DLO_HIP(nullptr, hipEventRecord(c->comp_done[i], c->gather_s));
   }
   if (!grow_pool(c, events_per_forward(c))) return fail(DLO_E_HIP, "trace event creation failed");
+  // the device address of the library's static scratch (dlo_forward_static),
+  // taken here, at set-up, with the context's device current
+  c->static_ws_err = static_scratch(c->device, &c->static_ws);
+  if (c->static_ws_err != hipSuccess) (void)hipGetLastError();
   DLO_HIP(nullptr, hipStreamSynchronize(c->gather_s));
   *out = ctx.release();
   return DLO_OK;
@@ -729,6 +735,29 @@ extern "C" DLO_API dlo_status dlo_forward(dlo_ctx* ctx, float* x, const float* c
   if (st == DLO_OK) st = check_loaded(ctx);
   if (st != DLO_OK) return st;
   return forward_impl(ctx, x, cond, tokens, stream, ctx->ws);
+}
+
+extern "C" DLO_API dlo_status dlo_forward_static(dlo_ctx* ctx, float* x, const float* cond, int32_t tokens,
+                                                 hipStream_t stream) {
+  clear_error();
+  dlo_status st = check_forward(ctx, x, cond, tokens);
+  if (st != DLO_OK) return st;
+  const size_t need = carve_workspace(nullptr, size_t(tokens), size_t(ctx->d_max), size_t(ctx->m_max),
+                                      ctx->mixed_width, nullptr);
+  if (need > kStaticScratchBytes)
+    return fail(DLO_E_INVAL, "%d tokens need %zu bytes of activation workspace; the static scratch holds %zu",
+                tokens, need, kStaticScratchBytes);
+  if (ctx->flags & (DLO_FLAG_TRACE | DLO_FLAG_TRACE_KERNELS))
+    return fail(DLO_E_STATE, "tracing creates timing events; clear the trace flags for dlo_forward_static");
+  if (ctx->static_ws == nullptr)
+    return fail(DLO_E_STATE, "the static scratch is unavailable on device %d: %s", ctx->device,
+                hipGetErrorString(ctx->static_ws_err));
+  st = check_loaded(ctx);
+  if (st != DLO_OK) return st;
+  Workspace w;
+  carve_workspace(static_cast<char*>(ctx->static_ws), size_t(tokens), size_t(ctx->d_max), size_t(ctx->m_max),
+                  ctx->mixed_width, &w);
+  return forward_impl(ctx, x, cond, tokens, stream, w);
 }
 
 extern "C" DLO_API dlo_status dlo_destroy(dlo_ctx* ctx) {

@@ -203,6 +203,14 @@ hipError_t launch_attention(const uint16_t*, int, const uint16_t*, int, uint16_t
   return hipSuccess;
 }
 
+// The library's static device scratch: the fake kernels never touch the
+// workspace, so a small host buffer stands in for it.
+hipError_t static_scratch(int, void** out) {
+  alignas(256) static unsigned char buf[4096];
+  *out = buf;
+  return hipSuccess;
+}
+
 }  // namespace dlo
 
 namespace {
