@@ -55,10 +55,15 @@ namespace {
 
 constexpr size_t kAlign = 256;
 // Default H2D chunk: min(largest shard, a quarter of the largest padded block,
-// 2^24 elements = 32 MiB).  The two landing buffers then add at most half a
-// block, and at most 64 MiB, to the two slots' weight bytes: slots + landing
-// <= 2.5 x the largest block at any dp.
-constexpr int64_t kDefaultChunk = int64_t(1) << 24;
+// 2^26 elements = 128 MiB).  The two landing buffers then add at most half a
+// block, and at most 256 MiB, to the two slots' weight bytes: slots + landing
+// <= 2.5 x the largest block at any dp.  Transfers of 128 MiB keep the host
+// link busier than 32 MiB ones while the compute stream holds every CU (each
+// transfer's reconstruction waits for CUs to free up, and the next transfer
+// into that landing buffer waits for the reconstruction): 8 blocks of the
+// d 8192 workload stream in 241.7 ms with 128 MiB transfers, 256.1 ms with
+// 32 MiB ones.
+constexpr int64_t kDefaultChunk = int64_t(1) << 26;
 constexpr int64_t kMinChunk = 4096;
 constexpr int kLandSlack = 8;  // landing offset (elements) used to co-align with the slot
 constexpr size_t kMaxTraceEvents = size_t(1) << 20;  // bound on recorded trace events per context
