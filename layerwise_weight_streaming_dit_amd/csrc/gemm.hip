@@ -404,6 +404,354 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 256x256 tile with ONE wave per SIMD (four waves).  The waves split the
+// tile along the dimension of the activation operand, so each wave owns its
+// own slice of the weight operand and widens every weight fragment it uses
+// exactly once per k slice (no two waves widen the same weights):
+//   WM=1, WN=4: waves own 64 weight rows (columns of C), 256x64 per wave;
+//   WM=4, WN=1: the transposed v projection (weights are the A operand),
+//               waves own 64 weight rows, 64x256 per wave.
+// Per 64-wide K step a wave issues 64 MFMAs (256 fp32 accumulators per lane
+// in the accumulation registers) against 40 fragment reads, and widens 8
+// weight fragments.  With no second wave on the SIMD the stream is
+// pipelined by hand:
+//   * fragments of k slice j+1 are read while slice j multiplies, and the
+//     weight fragments among them are widened to fp16 a few MFMAs later,
+//     between MFMAs, so no MFMA waits for a conversion;
+//   * the step's barrier sits before the last slice's MFMAs: every wave has
+//     read all four slices of the stage by then and waited for its loads of
+//     the next step, so after the barrier the next stage is complete and this
+//     one may be overwritten;
+//   * the loads of step kt+2 into the stage just released start right after
+//     that barrier (ten during the last slice, six during the next step's
+//     first slice), so they have three slices to land;
+//   * load addresses are a uniform base (scalar registers, advanced per step)
+//     plus a fixed per-lane offset; the LDS destination of every load is
+//     uniform too, so issuing a load costs no vector instruction.
+template <int WM, int WN, int EPI>
+__global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
+  constexpr int BM = 256, BN = 256, W = 4;
+  static_assert(WM * WN == W, "four waves");
+  constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
+  constexpr int STAGE = BM * kBK;   // elements per operand per stage (32 KB)
+  constexpr int LA = BM / 8 / W;    // 1 KB DMA loads per wave per operand per stage (8)
+  constexpr int ND = 2 * LA;        // DMA loads per wave per step (16)
+  constexpr bool A_IS_WEIGHT = EPI == EPI_VT_F16;
+  constexpr int NWF = A_IS_WEIGHT ? TM : TN;  // weight fragments per slice
+  static_assert(NWF == 2, "each wave owns 64 weight rows");
+  static_assert(WTM % 64 == 0 && WTN % 64 == 0, "fragment addressing assumes an even tile count per wave");
+
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB1[STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
+  const int wm = wave / WN, wn = wave % WN;
+
+  // ---- tile order: XCD-contiguous ranges, grouped along M
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int nb = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, local = bid >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  const int logical = (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  const int group_span = kGroupM * tiles_n;
+  const int group = logical / group_span;
+  const int first_m = group * kGroupM;
+  const int gsz = min(tiles_m - first_m, kGroupM);
+  const int in_group = logical - group * group_span;
+  const int tile_m = first_m + in_group % gsz;
+  const int tile_n = in_group / gsz;
+  const int m0 = tile_m * BM, n0 = tile_n * BN;
+
+  // ---- DMA sources: per-lane byte offsets (rows clamped in bounds) from a
+  // uniform base; LDS slot s of a stage holds row s / 8, 16-byte chunk
+  // (s % 8) ^ swz(row)
+  uint32_t ga[LA], gb[LA];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int slot = (wave * LA + i) * 64 + lane, row = slot >> 3;
+    const int c = (slot & 7) ^ swz(row);
+    ga[i] = (static_cast<uint32_t>(min(m0 + row, g.M - 1)) * g.lda + c * 8) * 2u;
+    gb[i] = (static_cast<uint32_t>(min(n0 + row, g.w_rows - 1)) * g.ldw + c * 8) * 2u;
+  }
+  const int nk = g.K / kBK;
+
+  auto stageA = [&](auto S) -> uint16_t* {
+    if constexpr (decltype(S)::value == 0) return sA0;
+    else return sA1;
+  };
+  auto stageB = [&](auto S) -> uint16_t* {
+    if constexpr (decltype(S)::value == 0) return sB0;
+    else return sB1;
+  };
+  // DMA load d (< ND) of K step `kstep` (clamped) into stage S
+  auto issue_one = [&](auto S, int kstep, int d) {
+    const int ks = min(kstep, nk - 1) * kBK;  // uniform element offset
+    if (d < LA)
+      dma16(at(g.a + ks, ga[d]), stageA(S) + (wave * LA + d) * 512);
+    else
+      dma16(at(g.w + ks, gb[d - LA]), stageB(S) + (wave * LA + d - LA) * 512);
+  };
+
+  f32x16_t acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
+
+  // Fragment pipeline: raw fragments double-buffered by slice parity
+  // (four slices per step: parities 0, 1, 0, 1); wc holds the widened
+  // weight fragments.
+  bf16x8_t ra[2][TM], rb[2][TN];
+  f16x8_t wc[2][NWF];
+  // Fragment addresses.  Tile rows are 32 apart, so within a wave's rows
+  // (which start at a multiple of 32) the chunk swizzle of fragment row
+  // R + (lane % 32) is swz(lane % 32) ^ 4 for odd tiles and swz(lane % 32) for
+  // even ones: per k slice two per-lane offsets serve every tile, the tile
+  // itself being a constant offset.
+  int fo[4][2];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int l = lane & 31;
+      fo[ks][par] = l * kBK + ((((ks * 2 + (lane >> 5)) ^ swz(l)) ^ (4 * par)) << 3);
+    }
+  const int arow0 = wm * WTM * kBK, brow0 = wn * WTN * kBK;  // uniform
+  auto read_frags = [&](auto S, int ks, auto P) {
+    constexpr int p = decltype(P)::value;
+    const uint16_t* a = stageA(S) + arow0;
+    const uint16_t* b = stageB(S) + brow0;
+    auto rd_a = [&] {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+        ra[p][tm] = *reinterpret_cast<const bf16x8_t*>(a + tm * 32 * kBK + fo[ks][tm & 1]);
+    };
+    auto rd_b = [&] {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+        rb[p][tn] = *reinterpret_cast<const bf16x8_t*>(b + tn * 32 * kBK + fo[ks][tn & 1]);
+    };
+    // the weight fragments first: their widening waits only for them
+    if constexpr (A_IS_WEIGHT) {
+      rd_a();
+      rd_b();
+    } else {
+      rd_b();
+      rd_a();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // widen dword q (0..3) of weight fragment f of parity P
+  auto widen_part = [&](auto P, int f, int q) {
+    constexpr int p = decltype(P)::value;
+    const u32x4_t w = __builtin_bit_cast(u32x4_t, A_IS_WEIGHT ? ra[p][f] : rb[p][f]);
+    u32x4_t o = __builtin_bit_cast(u32x4_t, wc[p][f]);
+    o[q] = pack_f16x2(__uint_as_float(w[q] << 16), __uint_as_float(w[q] & 0xffff0000u));
+    wc[p][f] = __builtin_bit_cast(f16x8_t, o);
+  };
+  // The 16 MFMAs of the slice of parity P; after MFMA i, dma(i) and, for
+  // i = 4, 6, ..., 14, a quarter of a weight fragment of parity P ^ 1 (whose
+  // reads were issued at the start of the slice).
+  auto mfma_slice = [&](auto P, auto&& dma) {
+    constexpr int p = decltype(P)::value;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      // weight fragment outer, so each widened fragment is done with early
+      const int wf = i / (16 / NWF), af = i % (16 / NWF);
+      const int tm = A_IS_WEIGHT ? wf : af, tn = A_IS_WEIGHT ? af : wf;
+      const f16x8_t a16 = A_IS_WEIGHT ? wc[p][tm] : __builtin_bit_cast(f16x8_t, ra[p][tm]);
+      const f16x8_t b16 = A_IS_WEIGHT ? __builtin_bit_cast(f16x8_t, rb[p][tn]) : wc[p][tn];
+      acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b16, a16, acc[tm][tn], 0, 0, 0);
+      dma(i);
+      if (i >= 4 && (i & 1) == 0) {
+        const int j = (i - 4) / 2;  // 0..5: eight quarter fragments
+        widen_part(IC<p ^ 1>{}, j < 4 ? 0 : 1, j & 3);
+        if (j >= 4) widen_part(IC<p ^ 1>{}, 1, (j & 3) + 2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the next slice's reads landed during these MFMAs: retiring them here
+    // costs nothing and keeps the LDS counter exact for the next slice
+    wait_lgkmcnt0();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  constexpr int NEARLY = 10;
+  auto step = [&](auto S, int kt) {
+    constexpr int s = decltype(S)::value;
+    auto dma_range = [&](auto T, int kstep, int first, int count) {
+      return [&, T, kstep, first, count](int i) {
+        if (i < count) issue_one(T, kstep, first + i);
+      };
+    };
+    auto none = [](int) {};
+    read_frags(S, 1, IC<1>{});
+    mfma_slice(IC<0>{}, dma_range(IC<s ^ 1>{}, kt + 1, NEARLY, ND - NEARLY));
+    read_frags(S, 2, IC<0>{});
+    mfma_slice(IC<1>{}, none);
+    read_frags(S, 3, IC<1>{});
+    mfma_slice(IC<0>{}, none);
+    // step kt+1's loads have landed and slice 3 is in registers and widened:
+    // publish the next stage, release this one
+    wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(IC<s ^ 1>{}, 0, IC<0>{});
+    mfma_slice(IC<1>{}, dma_range(S, kt + 2, 0, NEARLY));
+  };
+
+#pragma unroll
+  for (int d = 0; d < ND; ++d) issue_one(IC<0>{}, 0, d);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  read_frags(IC<0>{}, 0, IC<0>{});
+#pragma unroll
+  for (int d = 0; d < NEARLY; ++d) issue_one(IC<1>{}, 1, d);
+  wait_lgkmcnt0();
+#pragma unroll
+  for (int f = 0; f < NWF; ++f)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) widen_part(IC<0>{}, f, q);
+  // K is a multiple of two steps (128), so the ring unrolls without early exits
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(IC<0>{}, kt);
+    step(IC<1>{}, kt + 1);
+  }
+  wait_vmcnt<0>();  // drain the clamped tail loads before the epilogue
+  __syncthreads();  // every wave is done with the stage buffers
+  // keep the accumulator reads below (spilling them otherwise)
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- epilogue through LDS (each wave its own 32 KB region), one 32-row
+  // tile row per pass.  Each 32x32 accumulator is a tile of C^T: lane l owns
+  // output row (l % 32) of the tile and, for q = 0..3, the four consecutive
+  // columns 8q + 4(l / 32) + 0..3.
+  uint16_t* region = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sB0 : sB1;
+  const bool interior = m0 + BM <= g.M && n0 + BN <= g.N;
+  const int row0 = m0 + wm * WTM, col0 = n0 + wn * WTN;
+  if constexpr (EPI == EPI_GATED_F32) {
+    // x = x + gate * (acc + bias): staged as fp32 rows of WTN (+4) floats,
+    // then whole row segments, the pass's x loads issued before its stores
+    constexpr int RS = WTN + 4, LPR = WTN / 4, RPI = 64 / LPR, NI = 32 / RPI;
+    float* fr = reinterpret_cast<float*>(region);
+    const int c4 = (lane % LPR) * 4, cc = col0 + c4;
+    const bool col_ok = cc < g.N;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = tn * 32 + 8 * q + 4 * (lane >> 5);
+          const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(g.bias + min(col0 + c, g.N - 4));
+          f32x4_t v;
+          v.x = acc[tm][tn][4 * q] + __uint_as_float(bb.x << 16);
+          v.y = acc[tm][tn][4 * q + 1] + __uint_as_float(bb.x & 0xffff0000u);
+          v.z = acc[tm][tn][4 * q + 2] + __uint_as_float(bb.y << 16);
+          v.w = acc[tm][tn][4 * q + 3] + __uint_as_float(bb.y & 0xffff0000u);
+          *reinterpret_cast<f32x4_t*>(fr + (lane & 31) * RS + c) = v;
+        }
+      const f32x4_t gt = *reinterpret_cast<const f32x4_t*>(g.gate + min(cc, g.N - 4));
+      // half a pass at a time: its x loads, then its stores
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4_t xr[NI / 2];
+#pragma unroll
+        for (int k = 0; k < NI / 2; ++k) {
+          const int row = row0 + tm * 32 + (h * NI / 2 + k) * RPI + lane / LPR;
+          const int64_t off = static_cast<int64_t>(interior ? row : min(row, g.M - 1)) * g.ldo +
+                              (interior ? cc : min(cc, g.N - 4));
+          xr[k] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(g.out) + off);
+        }
+#pragma unroll
+        for (int k = 0; k < NI / 2; ++k) {
+          const int r = (h * NI / 2 + k) * RPI + lane / LPR, row = row0 + tm * 32 + r;
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(fr + r * RS + c4);
+          if (interior || (row < g.M && col_ok))
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(g.out) + static_cast<int64_t>(row) * g.ldo + cc) =
+                xr[k] + gt * v;
+        }
+      }
+    }
+  } else {
+    // fp16 results: staged as rows of WTN (+8) halves, then whole row
+    // segments of 16 bytes per lane
+    constexpr int RS = WTN + 8, LPR = WTN / 8, RPI = 64 / LPR, NI = 32 / RPI;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4_t v;
+          v.x = acc[tm][tn][4 * q];
+          v.y = acc[tm][tn][4 * q + 1];
+          v.z = acc[tm][tn][4 * q + 2];
+          v.w = acc[tm][tn][4 * q + 3];
+          int c = tn * 32 + 8 * q + 4 * (lane >> 5);
+          if constexpr (EPI == EPI_VT_F16) {
+            // transposed v: per-row bias; tokens c..c+3 land at their
+            // permuted key positions, consecutive too (the tile's first
+            // column is a multiple of 16, and only bits 2 and 3 move)
+            v += bf16_to_f32(g.bias[min(row0 + tm * 32 + (lane & 31), g.M - 1)]);
+            c = vt_key_position(c);
+          } else {
+            const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(g.bias + min(col0 + c, g.N - 4));
+            v.x += __uint_as_float(bb.x << 16);
+            v.y += __uint_as_float(bb.x & 0xffff0000u);
+            v.z += __uint_as_float(bb.y << 16);
+            v.w += __uint_as_float(bb.y & 0xffff0000u);
+          }
+          if constexpr (EPI == EPI_BIAS_GELU_F16) {
+            v.x = gelu_tanh(v.x);
+            v.y = gelu_tanh(v.y);
+            v.z = gelu_tanh(v.z);
+            v.w = gelu_tanh(v.w);
+          }
+          u32x2_t w;
+          w.x = pack_f16x2(v.x, v.y);
+          w.y = pack_f16x2(v.z, v.w);
+          *reinterpret_cast<u32x2_t*>(region + (lane & 31) * RS + c) = w;
+        }
+#pragma unroll
+      for (int k = 0; k < NI; ++k) {
+        const int r = k * RPI + lane / LPR, c8 = (lane % LPR) * 8;
+        const u32x4_t val = *reinterpret_cast<const u32x4_t*>(region + r * RS + c8);
+        const int row = row0 + tm * 32 + r, cc = col0 + c8;
+        if (interior || (row < g.M && cc < g.N))
+          *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(g.out) + static_cast<int64_t>(row) * g.ldo + cc) = val;
+      }
+    }
+  }
+}
+
+hipError_t launch_wt(int epi, const GemmArgs& g, hipStream_t s) {
+  const int tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
+  const dim3 grid(tiles), block(256);
+  switch (epi) {
+    case EPI_BIAS_F16:
+      hipLaunchKernelGGL((gemm_wt_kernel<1, 4, EPI_BIAS_F16>), grid, block, 0, s, g);
+      break;
+    case EPI_BIAS_GELU_F16:
+      hipLaunchKernelGGL((gemm_wt_kernel<1, 4, EPI_BIAS_GELU_F16>), grid, block, 0, s, g);
+      break;
+    case EPI_GATED_F32:
+      hipLaunchKernelGGL((gemm_wt_kernel<1, 4, EPI_GATED_F32>), grid, block, 0, s, g);
+      break;
+    default:
+      hipLaunchKernelGGL((gemm_wt_kernel<4, 1, EPI_VT_F16>), grid, block, 0, s, g);
+      break;
+  }
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN, int PFD>
 hipError_t launch_shape(int epi, const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
@@ -428,12 +776,18 @@ hipError_t launch_shape(int epi, const GemmArgs& g, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm(int epilogue, const GemmArgs& g, hipStream_t s) {
-  // Largest tile that still gives every CU (256) at least one workgroup.  The
-  // 256x128 tile (4 waves, one per SIMD) pays off only over a long K; for
+  // Largest tile that still gives every CU (256) at least one workgroup.
+  // With four or more 256x256 tiles per CU the one-wave-per-SIMD kernel is
+  // ahead (measured on warm operands, same results bit for bit: 3-5% on the
+  // q,k / MLP GEMMs of the large and mid-video shapes, 11% on their
+  // transposed v projections); with one or two tiles per CU the eight-wave
+  // kernel's second wave per SIMD still hides more (image shapes: 1-3%).
+  // The 256x128 tile (4 waves, one per SIMD) pays off only over a long K; for
   // short K two 128x128 tiles per CU (8 waves) finish first (measured: 9%
   // faster at 2048x4096x2048, 4% slower at 4096x2048x8192).
   const int64_t t256 = static_cast<int64_t>((g.M + 255) / 256) * ((g.N + 255) / 256);
   const int64_t t256x128 = static_cast<int64_t>((g.M + 255) / 256) * ((g.N + 127) / 128);
+  if (t256 >= 1024) return launch_wt(epilogue, g, s);
   if (t256 >= 256) return launch_shape<256, 256, 2, 4, 0>(epilogue, g, s);
   if (t256x128 >= 256 && g.K >= 4096) return launch_shape<256, 128, 2, 2, 2>(epilogue, g, s);
   return launch_shape<128, 128, 2, 2, 0>(epilogue, g, s);
