@@ -240,7 +240,7 @@ def main():
     ap.add_argument("--chunk", type=int, default=0, help="H2D chunk in elements (0 = the library's default)")
     ap.add_argument("--gen-threads", type=int, default=12)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--cpu-min-blocks", type=int, default=2)
+    ap.add_argument("--cpu-min-blocks", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-serial", action="store_true")
     ap.add_argument("--timed-only", action="store_true",
