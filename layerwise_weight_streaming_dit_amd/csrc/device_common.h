@@ -75,12 +75,24 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane i's data lands
-// at lds + 16 * i (global_load_lds_dwordx4).  The LDS address-space cast only
-// exists in the device pass; the host pass sees an empty body.
-__device__ __forceinline__ void dma16(const uint16_t* gsrc, uint16_t* lds) {
+// Raw (byte-addressed, unswizzled) buffer descriptor over `bytes` bytes from
+// `base`; dword 3 selects the 32-bit data format of gfx9 raw buffer loads.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+// 16 bytes per lane from buffer offset voff + soff straight into LDS (lane i's
+// data lands at lds + 16 * i: buffer_load_dwordx4 ... lds, no staging
+// registers).  The LDS address-space cast only exists in the device pass.
+// Unlike global_load_lds (a FLAT-encoded access, which the compiler must
+// assume may complete out of order with LDS reads, so that after one every
+// wait it inserts for a fragment read becomes lgkmcnt(0)), a buffer load
+// counts on vmcnt only: the compiler's waits for fragment reads stay exact
+// and a wave starts multiplying as soon as its first fragments are in.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, uint16_t* lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 #endif
 }
 
@@ -93,11 +105,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // s_waitcnt lgkmcnt(0) leaving vmcnt / expcnt unconstrained.
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
-
-// base + 32-bit byte offset (lets the loads use an SGPR base with a VGPR offset)
-__device__ __forceinline__ const uint16_t* at(const uint16_t* base, uint32_t byte_off) {
-  return reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(base) + byte_off);
-}
 
 template <int V>
 using IC = std::integral_constant<int, V>;

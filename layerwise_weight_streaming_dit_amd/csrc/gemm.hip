@@ -9,7 +9,7 @@
 // A workgroup computes a BM x BN tile with WM x WN waves; each wave owns a
 // (BM / WM) x (BN / WN) sub-tile made of 32x32 MFMA tiles.  K advances in
 // steps of 64 through two LDS stages.  Global data moves straight into LDS
-// with gfx950's global_load_lds_dwordx4 (no staging registers), one step
+// with buffer_load_dwordx4 ... lds (no staging registers), one step
 // ahead of the MFMAs that consume it; each row's 64 k values are one full
 // 128-byte cache line, so every line is fetched from L2 once per tile.  One
 // barrier per step both publishes a landed stage and frees the other one.
@@ -112,6 +112,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
   }
   const int nk = g.K / kBK;
 
+  // buffer descriptors over each operand's extent (the host checks that it
+  // fits 32 bits); the per-lane offsets above never reach past it
+  const __amdgpu_buffer_rsrc_t rs_a = buffer_rsrc(g.a, (static_cast<uint32_t>(g.M - 1) * g.lda + g.K) * 2u);
+  const __amdgpu_buffer_rsrc_t rs_w = buffer_rsrc(g.w, (static_cast<uint32_t>(g.w_rows - 1) * g.ldw + g.K) * 2u);
+
   // L2 prefetch: one 4-byte DMA per 128-byte line (row) of a step's A and W
   // tiles, NPF per wave, landing in a scratch LDS word per lane that nothing
   // reads.  Lanes past the last row repeat it.
@@ -130,7 +135,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
     const uint32_t koff = static_cast<uint32_t>(min(kstep, nk - 1)) * (kBK * 2);
 #pragma unroll
     for (int j = 0; j < NPF; ++j) {
-      const uint16_t* src = pf_is_a[j] ? at(g.a, pf_off[j] + koff) : at(g.w, pf_off[j] + koff);
+      // a global (FLAT) load here measured 2% faster than a buffer load on
+      // the MLP-down shape (4096x2048x8192)
+      const char* src = reinterpret_cast<const char*>(pf_is_a[j] ? g.a : g.w) + pf_off[j] + koff;
 #if defined(__HIP_DEVICE_COMPILE__)
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)sPf, 4, 0, 0);
 #endif
@@ -151,9 +158,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
   auto issue_one = [&](auto S, int kstep, int d) {
     const uint32_t koff = static_cast<uint32_t>(min(kstep, nk - 1)) * (kBK * 2);
     if (d < LA)
-      dma16(at(g.a, ga[d] + koff), stageA(S) + (wave * LA + d) * 512);
+      dma16_buf(rs_a, ga[d], koff, stageA(S) + (wave * LA + d) * 512);
     else
-      dma16(at(g.w, gb[d - LA] + koff), stageB(S) + (wave * LB + d - LA) * 512);
+      dma16_buf(rs_w, gb[d - LA], koff, stageB(S) + (wave * LB + d - LA) * 512);
   };
   auto issue = [&](auto S, int kstep) {
 #pragma unroll
@@ -416,9 +423,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
 // in the accumulation registers) against 40 fragment reads, and widens 8
 // weight fragments.  With no second wave on the SIMD the stream is
 // pipelined by hand:
-//   * fragments of k slice j+1 are read while slice j multiplies, and the
-//     weight fragments among them are widened to fp16 a few MFMAs later,
-//     between MFMAs, so no MFMA waits for a conversion;
+//   * the fragments of k slice j+1 are read one after each of slice j's
+//     first ten MFMAs, and the weight fragments among them (read first) are
+//     widened to fp16 a few MFMAs later, between MFMAs, so no MFMA waits for
+//     a conversion; the stage loads are buffer loads (dma16_buf), so the
+//     compiler's waits for the reads are exact and each MFMA of the next
+//     slice waits only for its own fragments;
 //   * the step's barrier sits before the last slice's MFMAs: every wave has
 //     read all four slices of the stage by then and waited for its loads of
 //     the next step, so after the barrier the next stage is complete and this
@@ -487,13 +497,18 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
     if constexpr (decltype(S)::value == 0) return sB0;
     else return sB1;
   };
-  // DMA load d (< ND) of K step `kstep` (clamped) into stage S
+  // buffer descriptors over each operand's extent (the host checks that it
+  // fits 32 bits); the per-lane offsets above never reach past it
+  const __amdgpu_buffer_rsrc_t rs_a = buffer_rsrc(g.a, (static_cast<uint32_t>(g.M - 1) * g.lda + g.K) * 2u);
+  const __amdgpu_buffer_rsrc_t rs_w = buffer_rsrc(g.w, (static_cast<uint32_t>(g.w_rows - 1) * g.ldw + g.K) * 2u);
+  // DMA load d (< ND) of K step `kstep` (clamped) into stage S: per-lane
+  // offset plus the step's uniform byte offset
   auto issue_one = [&](auto S, int kstep, int d) {
-    const int ks = min(kstep, nk - 1) * kBK;  // uniform element offset
+    const uint32_t kb = static_cast<uint32_t>(min(kstep, nk - 1)) * (kBK * 2);
     if (d < LA)
-      dma16(at(g.a + ks, ga[d]), stageA(S) + (wave * LA + d) * 512);
+      dma16_buf(rs_a, ga[d], kb, stageA(S) + (wave * LA + d) * 512);
     else
-      dma16(at(g.w + ks, gb[d - LA]), stageB(S) + (wave * LA + d - LA) * 512);
+      dma16_buf(rs_w, gb[d - LA], kb, stageB(S) + (wave * LA + d - LA) * 512);
   };
 
   f32x16_t acc[TM][TN];
@@ -547,6 +562,18 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
     }
     __builtin_amdgcn_sched_barrier(0);
   };
+  // fragment read j (< TM + TN; the weight fragments first) of k slice ks of
+  // stage S into parity P
+  auto read_one = [&](auto S, int ks, auto P, int j) {
+    constexpr int p = decltype(P)::value;
+    constexpr int NW = A_IS_WEIGHT ? TM : TN;
+    const bool wfrag = j < NW;
+    const int t = wfrag ? j : j - NW;
+    if (A_IS_WEIGHT == wfrag)
+      ra[p][t] = *reinterpret_cast<const bf16x8_t*>(stageA(S) + arow0 + t * 32 * kBK + fo[ks][t & 1]);
+    else
+      rb[p][t] = *reinterpret_cast<const bf16x8_t*>(stageB(S) + brow0 + t * 32 * kBK + fo[ks][t & 1]);
+  };
   // widen dword q (0..3) of weight fragment f of parity P
   auto widen_part = [&](auto P, int f, int q) {
     constexpr int p = decltype(P)::value;
@@ -555,10 +582,12 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
     o[q] = pack_f16x2(__uint_as_float(w[q] << 16), __uint_as_float(w[q] & 0xffff0000u));
     wc[p][f] = __builtin_bit_cast(f16x8_t, o);
   };
-  // The 16 MFMAs of the slice of parity P; after MFMA i, dma(i) and, for
-  // i = 4, 6, ..., 14, a quarter of a weight fragment of parity P ^ 1 (whose
-  // reads were issued at the start of the slice).
-  auto mfma_slice = [&](auto P, auto&& dma) {
+  // The 16 MFMAs of the slice of parity P; after MFMA i, rd(i) (fragment
+  // read i of the next slice, into parity P ^ 1), dma(i) and, for i = 4, 6,
+  // ..., 14, a quarter of a weight fragment of parity P ^ 1 (read after MFMAs
+  // 0 and 1).  The compiler's LDS waits are exact (see dma16_buf): each MFMA
+  // waits only for its own fragments.
+  auto mfma_slice = [&](auto P, auto&& dma, auto&& rd) {
     constexpr int p = decltype(P)::value;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -568,6 +597,7 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
       const f16x8_t a16 = A_IS_WEIGHT ? wc[p][tm] : __builtin_bit_cast(f16x8_t, ra[p][tm]);
       const f16x8_t b16 = A_IS_WEIGHT ? __builtin_bit_cast(f16x8_t, rb[p][tn]) : wc[p][tn];
       acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b16, a16, acc[tm][tn], 0, 0, 0);
+      rd(i);
       dma(i);
       if (i >= 4 && (i & 1) == 0) {
         const int j = (i - 4) / 2;  // 0..5: eight quarter fragments
@@ -576,10 +606,6 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // the next slice's reads landed during these MFMAs: retiring them here
-    // costs nothing and keeps the LDS counter exact for the next slice
-    wait_lgkmcnt0();
-    __builtin_amdgcn_sched_barrier(0);
   };
 
   constexpr int NEARLY = 10;
@@ -591,20 +617,21 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
       };
     };
     auto none = [](int) {};
-    read_frags(S, 1, IC<1>{});
-    mfma_slice(IC<0>{}, dma_range(IC<s ^ 1>{}, kt + 1, NEARLY, ND - NEARLY));
-    read_frags(S, 2, IC<0>{});
-    mfma_slice(IC<1>{}, none);
-    read_frags(S, 3, IC<1>{});
-    mfma_slice(IC<0>{}, none);
+    auto reads = [&](auto T, int ks, auto P) {
+      return [&, T, ks, P](int i) {
+        if (i < TM + TN) read_one(T, ks, P, i);
+      };
+    };
+    mfma_slice(IC<0>{}, dma_range(IC<s ^ 1>{}, kt + 1, NEARLY, ND - NEARLY), reads(S, 1, IC<1>{}));
+    mfma_slice(IC<1>{}, none, reads(S, 2, IC<0>{}));
+    mfma_slice(IC<0>{}, none, reads(S, 3, IC<1>{}));
     // step kt+1's loads have landed and slice 3 is in registers and widened:
     // publish the next stage, release this one
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    read_frags(IC<s ^ 1>{}, 0, IC<0>{});
-    mfma_slice(IC<1>{}, dma_range(S, kt + 2, 0, NEARLY));
+    mfma_slice(IC<1>{}, dma_range(S, kt + 2, 0, NEARLY), reads(IC<s ^ 1>{}, 0, IC<0>{}));
   };
 
 #pragma unroll
@@ -777,18 +804,15 @@ hipError_t launch_shape(int epi, const GemmArgs& g, hipStream_t s) {
 
 hipError_t launch_gemm(int epilogue, const GemmArgs& g, hipStream_t s) {
   // Largest tile that still gives every CU (256) at least one workgroup.
-  // With four or more 256x256 tiles per CU the one-wave-per-SIMD kernel is
-  // ahead (measured on warm operands, same results bit for bit: 3-5% on the
-  // q,k / MLP GEMMs of the large and mid-video shapes, 11% on their
-  // transposed v projections); with one or two tiles per CU the eight-wave
-  // kernel's second wave per SIMD still hides more (image shapes: 1-3%).
-  // The 256x128 tile (4 waves, one per SIMD) pays off only over a long K; for
-  // short K two 128x128 tiles per CU (8 waves) finish first (measured: 9%
-  // faster at 2048x4096x2048, 4% slower at 4096x2048x8192).
+  // From one 256x256 tile per CU up, the one-wave-per-SIMD kernel is ahead
+  // (measured on warm operands, same results bit for bit: 1-9% on the image
+  // shapes with one or two tiles per CU, 5-10% on the large and mid-video
+  // shapes).  The 256x128 tile (4 waves, one per SIMD) pays off only over a
+  // long K; for short K two 128x128 tiles per CU (8 waves) finish first
+  // (measured: 9% faster at 2048x4096x2048, 4% slower at 4096x2048x8192).
   const int64_t t256 = static_cast<int64_t>((g.M + 255) / 256) * ((g.N + 255) / 256);
   const int64_t t256x128 = static_cast<int64_t>((g.M + 255) / 256) * ((g.N + 127) / 128);
-  if (t256 >= 1024) return launch_wt(epilogue, g, s);
-  if (t256 >= 256) return launch_shape<256, 256, 2, 4, 0>(epilogue, g, s);
+  if (t256 >= 256) return launch_wt(epilogue, g, s);
   if (t256x128 >= 256 && g.K >= 4096) return launch_shape<256, 128, 2, 2, 2>(epilogue, g, s);
   return launch_shape<128, 128, 2, 2, 0>(epilogue, g, s);
 }
