@@ -86,7 +86,9 @@ DLO_API dlo_status dlo_op_gemm(int32_t epilogue, const uint16_t* a, int32_t lda,
  * v[s][c] = vt[c*ld_vt + p(s)], p(s) = s with bits 2 and 3 swapped (so the
  * eight keys one lane multiplies are one aligned 16-byte run); ld_vt >=
  * tokens rounded up to 64, a multiple of 64, and the columns that hold keys
- * >= tokens finite.  hd = head_dim in {64, 128}. */
+ * >= tokens finite.  hd = head_dim in {64, 128}.  The q/k extent
+ * ((tokens - 1) * ld_qk + 2 * heads * hd) and the v^T extent
+ * (heads * hd * ld_vt) must each stay within 4 GiB (DLO_E_SHAPE otherwise). */
 DLO_API dlo_status dlo_op_attention(const uint16_t* qk, int32_t ld_qk, const uint16_t* vt,
                                     int32_t ld_vt, uint16_t* o, int32_t ld_o, int32_t tokens,
                                     int32_t heads, int32_t head_dim, hipStream_t stream);

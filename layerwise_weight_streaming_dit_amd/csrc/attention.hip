@@ -31,8 +31,10 @@
 //
 // Tiles: 256 queries (8 waves, two per SIMD) per workgroup and one workgroup
 // per CU, so each K/V tile fetched from L2 feeds 256 queries; 64 keys per
-// step, K and V^T double-buffered in LDS with XOR-swizzled 16-byte chunks; the
-// next tile's global loads are issued before the current tile's MFMAs.
+// step, K and V^T double-buffered in LDS with XOR-swizzled 16-byte chunks.
+// The next tile moves from global memory straight into LDS (buffer loads
+// with the LDS destination, no staging registers) while the current tile is
+// processed; one barrier per step publishes it.
 #include <math.h>
 
 #include <type_traits>
@@ -65,15 +67,13 @@ __global__ __launch_bounds__(BQ * 2, BQ == 256 ? 1 : 2) void attention_kernel(
   // with row % 16; 128-byte rows (V^T, and K for hd 64) pair rows r and r + 8
   // in the same half of a bank row, so they also XOR with row / 8.
   auto swz = [](int row, int nch) { return nch >= 16 ? (row & 15) : ((row ^ (row >> 3)) & 7); };
-  constexpr int NK = kBKV * KCH / kAttnThreads;  // K chunks per thread per step
-  constexpr int NV = HD * 8 / kAttnThreads;      // V^T chunks per thread per step
   constexpr int NKK = HD / 16;                    // MFMA k-steps over the head dim
   constexpr int NIB = HD / 32;                    // 32-row blocks of O^T
 
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBKV * HD];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][HD * kBKV];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5;
   const int kc = lane & 31;
   // Workgroups are dispatched round-robin over the 8 XCDs (workgroup i to XCD
@@ -103,38 +103,50 @@ __global__ __launch_bounds__(BQ * 2, BQ == 256 ? 1 : 2) void attention_kernel(
     for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const f16x8_t*>(qp + kk * 16);
   }
 
-  // Staging addresses.
-  int k_row[NK], k_chunk[NK], k_lds[NK], v_lds[NV];
-  const uint16_t* v_src[NV];
+  // Staging: every 1 KB block of a K or V^T tile is one DMA load of one wave
+  // (64 lanes x 16 bytes, contiguous in LDS), so the chunk swizzle is applied
+  // on the global side.  K blocks hold 512 / HD rows of HD values, V^T blocks
+  // 8 rows of 64 keys.  Per-lane byte offsets: the K row is clamped to the
+  // last token in the last tile; V^T columns past the last token exist
+  // (ld_vt covers whole 64-key tiles).
+  constexpr int NKB = HD / 8, NVBLK = HD / 8;  // 1 KB blocks per tile (K, V^T)
+  constexpr int NW = kAttnThreads / 64;
+  constexpr int LPW = (NKB + NVBLK) / NW;       // loads per wave per tile
+  static_assert(LPW * NW == NKB + NVBLK, "loads per wave");
+  constexpr int KRB = 512 / HD;                // K rows per block
+  const __amdgpu_buffer_rsrc_t rs_qk =
+      buffer_rsrc(qk, (static_cast<uint32_t>(T - 1) * ld_qk + static_cast<uint32_t>(2 * H * HD)) * 2u);
+  const __amdgpu_buffer_rsrc_t rs_vt =
+      buffer_rsrc(vt, (static_cast<uint32_t>(H * HD - 1) * ld_vt + static_cast<uint32_t>(ld_vt)) * 2u);
+  int ld_row[LPW];
+  uint32_t ld_col[LPW];  // K: row in the tile and byte column; V^T: byte offset
+  uint32_t ld_lds[LPW];
 #pragma unroll
-  for (int i = 0; i < NK; ++i) {
-    const int q = tid + i * kAttnThreads, j = q / KCH, c = q % KCH;
-    k_row[i] = j;
-    k_chunk[i] = c;
-    k_lds[i] = j * HD + ((c ^ swz(j, KCH)) << 3);
-  }
-#pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int q = tid + i * kAttnThreads, row = q >> 3, c = q & 7;
-    v_src[i] = vt + (static_cast<int64_t>(h) * HD + row) * ld_vt + c * 8;
-    v_lds[i] = row * kBKV + ((c ^ swz(row, 8)) << 3);
-  }
-
-  u32x4_t rk[NK], rv[NV];
-  auto load_tile = [&](int key0) {
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int key = min(key0 + k_row[i], T - 1);
-      rk[i] = *reinterpret_cast<const u32x4_t*>(qk + static_cast<int64_t>(key) * ld_qk + kcol + k_chunk[i] * 8);
+  for (int i = 0; i < LPW; ++i) {
+    const int b = wave * LPW + i;
+    if (b < NKB) {
+      const int row = b * KRB + lane / KCH, slot = lane % KCH;
+      ld_row[i] = row;
+      ld_col[i] = static_cast<uint32_t>(kcol + ((slot ^ swz(row, KCH)) << 3)) * 2u;
+      ld_lds[i] = b * 512;
+    } else {
+      const int vb = b - NKB, row = vb * 8 + lane / 8, slot = lane % 8;
+      ld_row[i] = 0;
+      ld_col[i] = (static_cast<uint32_t>(h * HD + row) * ld_vt + ((slot ^ swz(row, 8)) << 3)) * 2u;
+      ld_lds[i] = vb * 512;
     }
+  }
+  auto load_tile = [&](int key0, int kbuf, int vbuf) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i) rv[i] = *reinterpret_cast<const u32x4_t*>(v_src[i] + key0);
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < NK; ++i) *reinterpret_cast<u32x4_t*>(&sK[buf][k_lds[i]]) = rk[i];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) *reinterpret_cast<u32x4_t*>(&sV[buf][v_lds[i]]) = rv[i];
+    for (int i = 0; i < LPW; ++i) {
+      const int b = wave * LPW + i;  // uniform
+      if (b < NKB) {
+        const uint32_t voff = static_cast<uint32_t>(min(ld_row[i], T - 1 - key0)) * ld_qk * 2u + ld_col[i];
+        dma16_buf(rs_qk, voff, static_cast<uint32_t>(key0) * ld_qk * 2u, &sK[kbuf][ld_lds[i]]);
+      } else {
+        dma16_buf(rs_vt, ld_col[i], static_cast<uint32_t>(key0) * 2u, &sV[vbuf][ld_lds[i]]);
+      }
+    }
   };
 
   f32x16_t oacc[NIB];
@@ -217,16 +229,16 @@ __global__ __launch_bounds__(BQ * 2, BQ == 256 ? 1 : 2) void attention_kernel(
   };
 
   const int ntiles = (T + kBKV - 1) / kBKV;
-  load_tile(0);
-  store_tile(0);
+  load_tile(0, 0, 0);
+  wait_vmcnt<0>();
   __syncthreads();
 
   // every tile but the last: no key masking
   for (int t = 0; t + 1 < ntiles; ++t) {
     const int cur = t & 1;
-    load_tile((t + 1) * kBKV);
+    load_tile((t + 1) * kBKV, cur ^ 1, cur ^ 1);
     process(std::false_type{}, t, cur);
-    store_tile(cur ^ 1);
+    wait_vmcnt<0>();
     __syncthreads();
   }
   // the last tile, masked only if it is partial

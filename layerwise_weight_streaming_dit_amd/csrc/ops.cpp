@@ -94,6 +94,10 @@ extern "C" DLO_API dlo_status dlo_op_attention(const uint16_t* qk, int32_t ld_qk
   if (ld_o < d || ld_o % 4) return fail(DLO_E_SHAPE, "ld_o %d must be >= d and a multiple of 4", ld_o);
   const int64_t tp = (int64_t(tokens) + 63) / 64 * 64;
   if (ld_vt < tp || ld_vt % 64) return fail(DLO_E_SHAPE, "ld_vt %d must be >= %lld and a multiple of 64", ld_vt, (long long)tp);
+  // the kernel addresses q, k and v^T with 32-bit byte offsets
+  if ((int64_t(tokens - 1) * ld_qk + 2 * d) * 2 > int64_t(UINT32_MAX) || d * ld_vt * 2 > int64_t(UINT32_MAX))
+    return fail(DLO_E_SHAPE, "operand extent beyond 4 GiB (tokens %d x ld_qk %d, d %lld x ld_vt %d)", tokens, ld_qk,
+                (long long)d, ld_vt);
   if (!aligned(qk, 16) || !aligned(vt, 16) || !aligned(o, 8)) return fail(DLO_E_INVAL, "misaligned pointer");
   return launched(launch_attention(qk, ld_qk, vt, ld_vt, o, ld_o, tokens, heads, head_dim, s), "attention");
 }

@@ -280,6 +280,9 @@ void check_other_ops() {
   CHECK(dlo_op_attention(qk, 4096, vt, 4160, o, 2048, 4100, 16, 96, nullptr) == DLO_E_SHAPE);
   CHECK(dlo_op_attention(qk, 4000, vt, 4160, o, 2048, 4100, 16, 128, nullptr) == DLO_E_SHAPE);  // ld_qk < 2d
   CHECK(dlo_op_attention(qk, 4096, vt, 4160, o, 2048, 0, 16, 128, nullptr) == DLO_E_SHAPE);
+  // q/k or v^T extent beyond 4 GiB (32-bit byte offsets in the kernel)
+  CHECK(dlo_op_attention(qk, 1 << 17, vt, 1 << 17, o, 2048, 1 << 15, 16, 128, nullptr) == DLO_E_SHAPE);
+  CHECK(dlo_op_attention(qk, 4096, vt, 1 << 20, o, 2048, 4100, 16, 128, nullptr) == DLO_E_SHAPE);
   CHECK(g_seen.calls == 1);
 }
 
