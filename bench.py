@@ -7,7 +7,9 @@ A step is one streamed forward over every block of the workload (H2D of all
 dp shards of every block, on-GPU reconstruction into one of two slots, and
 the DiT block from the other slot), for one batch of synthetic input whose
 weights already sit in pinned host memory and whose activations already sit
-in HBM.  W untimed steps, then K timed steps between two device syncs.
+in HBM; for the irregular workload a step is its four sequential requests
+(four forwards with their drawn token counts).  W untimed steps, then K timed
+steps between two device syncs.
 
 The default workload is the largest one: 80 blocks of d 8192 (about 131 GB of
 bf16 weights, held only in pinned host memory).  Its weights are drawn block by
@@ -240,7 +242,7 @@ def main():
     ap.add_argument("--chunk", type=int, default=0, help="H2D chunk in elements (0 = the library's default)")
     ap.add_argument("--gen-threads", type=int, default=12)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--cpu-min-blocks", type=int, default=1)
+    ap.add_argument("--cpu-min-blocks", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-serial", action="store_true")
     ap.add_argument("--timed-only", action="store_true",
@@ -275,7 +277,10 @@ def main():
     wl = synth.workload(args.workload)
     shapes = list(wl.blocks)[: args.blocks] if args.blocks > 0 else list(wl.blocks)
     dp = args.dp or wl.dp_sizes[0]
-    T = wl.tokens
+    # a step of the irregular workload is its four sequential requests, each
+    # with its own drawn token count; every other workload runs one request
+    Ts = synth.request_tokens() if wl.name == "irregular" else [wl.tokens]
+    T = max(Ts)
     L = len(shapes)
     dev = torch.device("cuda:0")
     numels = [dlo.block_layout(s, dp)[0] for s in shapes]
@@ -328,11 +333,12 @@ def main():
 
     def step():
         for _ in range(repeats):
-            ctx.forward(xbuf, cond, T)
+            for t_req in Ts:
+                ctx.forward(xbuf, cond, t_req)
 
     # ---- timed region: HIP events only on the compute stream (around each
     # kernel), created before timing starts
-    ctx.reserve_trace((args.warmup + args.steps) * repeats)
+    ctx.reserve_trace((args.warmup + args.steps) * repeats * len(Ts))
     for i in range(args.warmup):
         step()
         torch.cuda.synchronize()
@@ -351,6 +357,13 @@ def main():
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (events {ev0.elapsed_time(ev1) / args.steps:.3f})")
     ktr = ctx.trace()
 
+    # token count of each traced forward (the timed forwards cycle through
+    # the requests in order)
+    f_first = min((r["forward"] for r in ktr), default=0)
+
+    def t_of(r):
+        return Ts[(r["forward"] - f_first) % len(Ts)]
+
     kernels = {}
     by = {}
     for r in ktr:
@@ -366,7 +379,7 @@ def main():
         # work per launch follows each launch's block (widths differ between
         # blocks in the irregular workload); average work / average time
         unit = kernel_work(shapes[0], T)[kind][0]
-        work = sum(kernel_work(shapes[r["block"]], T)[kind][1] for r in rs) / len(rs)
+        work = sum(kernel_work(shapes[r["block"]], t_of(r))[kind][1] for r in rs) / len(rs)
         e = {"launches": len(rs), "avg_ms": avg, "median_ms": med, "max_ms": ds[-1], "total_ms": sum(ds),
              "work_per_launch": work, "desc": KERNEL_DESC[kind]}
         if unit == "flop":
@@ -427,8 +440,8 @@ def main():
         ctx.set_flags(dlo.FLAG_TRACE | dlo.FLAG_TRACE_SPAN)
         ctx.reserve_trace(2)
         torch.cuda.synchronize()
-        for _ in range(2):
-            ctx.forward(xbuf, cond, T)
+        for i in range(2):
+            ctx.forward(xbuf, cond, Ts[i % len(Ts)])
         torch.cuda.synchronize()
         st = ctx.stats()
         tr = ctx.trace()
@@ -497,7 +510,7 @@ def main():
     if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
         cpu = cpu_baseline(wl, shapes, T, W_keep, args.cpu_seconds, args.cpu_min_blocks)
 
-    value = L * args.steps / elapsed
+    value = L * len(Ts) * args.steps / elapsed
     shp = shapes[0]
     h2d_per_step = st_all["h2d_bytes_per_forward"] * repeats
     out = {
@@ -518,11 +531,12 @@ def main():
         "config": {"workload": wl.description + (f"; first {L} of {wl.num_blocks} blocks streamed"
                                                  if L < wl.num_blocks else "") + note,
                    "blocks": L, "d_model": shp.d_model, "heads": shp.n_heads,
-                   "d_mlp": shp.d_mlp, "d_cond": shp.d_cond, "tokens": T, "batch": 1, "dp_size": dp,
+                   "d_mlp": shp.d_mlp, "d_cond": shp.d_cond, "tokens": T if len(Ts) == 1 else Ts,
+                   "batch": 1, "dp_size": dp,
                    "slots": 2, "pinned_host_bytes": pinned_bytes, "parallelism": "single GPU"},
-        "tokens_per_s": T * args.steps / elapsed,
-        "token_blocks_per_s": T * L * args.steps / elapsed,
-        "h2d_GBps_effective": h2d_per_step * args.steps / elapsed / 1e9,
+        "tokens_per_s": sum(Ts) * args.steps / elapsed,
+        "token_blocks_per_s": sum(Ts) * L * args.steps / elapsed,
+        "h2d_GBps_effective": h2d_per_step * len(Ts) * args.steps / elapsed / 1e9,
         "h2d_GBps_busy": sched["h2d_GBps_busy"] if sched else None,
         "h2d_ceiling_GBps": h2d_ceiling,
         "h2d_frac_of_pcie5_x16": (sched["h2d_GBps_busy"] / PCIE5_X16_GBPS) if sched else None,
