@@ -381,7 +381,12 @@ def main():
         unit = kernel_work(shapes[0], T)[kind][0]
         work = sum(kernel_work(shapes[r["block"]], t_of(r))[kind][1] for r in rs) / len(rs)
         e = {"launches": len(rs), "avg_ms": avg, "median_ms": med, "max_ms": ds[-1], "total_ms": sum(ds),
-             "work_per_launch": work, "desc": KERNEL_DESC[kind]}
+             "work_per_launch": work, "desc": KERNEL_DESC[kind],
+             "launches_over_1_5x_median": sum(1 for x in ds if x > 1.5 * med),
+             # the slowest launches: (timed step, block, ms)
+             "slowest": [[(r["forward"] - f_first) // (len(Ts) * max(repeats, 1)), r["block"],
+                          round(r["end"] - r["start"], 4)]
+                         for r in sorted(rs, key=lambda r: r["start"] - r["end"])[:4]]}
         if unit == "flop":
             e["TFLOPs"] = work / (avg * 1e-3) / 1e12
             e["mfma_frac"] = e["TFLOPs"] / PEAK_BF16_TFLOPS
