@@ -127,7 +127,7 @@ typedef struct dlo_config {
   const dlo_block_desc* blocks;/* num_blocks entries, copied by dlo_create */
   int32_t dp_size;             /* number of shards per block, >= 1 */
   int32_t max_tokens;          /* largest token count dlo_forward accepts, in [1, 2^20], and
-                                  max_tokens * max(d_model, d_mlp) * 2 bytes below 4 GiB */
+                                  max_tokens * max(2 * d_model, d_mlp) * 2 bytes below 4 GiB */
   int64_t landing_chunk_elems; /* largest H2D chunk in elements; 0 = default
                                   min(S_max, ceil(dp * S_max / 4), 2^26) with
                                   S_max the largest shard (the two landing

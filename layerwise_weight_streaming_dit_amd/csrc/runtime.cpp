@@ -265,9 +265,10 @@ dlo_status compute_sizes(const dlo_config* cfg, Sizes* z) {
     z->m_max = std::max(z->m_max, cfg->blocks[i].d_mlp);
     if (cfg->blocks[i].d_model != cfg->blocks[0].d_model) z->mixed = true;
   }
-  // GEMM operands are addressed with 32-bit byte offsets: the widest
-  // activation operand (tokens x max(d_model, d_mlp) fp16) must stay below 4 GiB.
-  if (size_t(cfg->max_tokens) * size_t(std::max(z->d_max, z->m_max)) * 2 > size_t(UINT32_MAX))
+  // GEMM and attention operands are addressed with 32-bit byte offsets: the
+  // widest activation operand (tokens x max(2 d_model, d_mlp) fp16: the q,k
+  // projection output or the MLP hidden layer) must stay below 4 GiB.
+  if (size_t(cfg->max_tokens) * size_t(std::max(2 * z->d_max, z->m_max)) * 2 > size_t(UINT32_MAX))
     return fail(DLO_E_INVAL, "max_tokens %d too large for the widest block (activations beyond 4 GiB)",
                 cfg->max_tokens);
   // largest padded block, dp * S_max elements: no chunk needs to be longer

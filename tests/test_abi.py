@@ -123,6 +123,11 @@ def test_activations_beyond_4gib_rejected():
     cfg, keep = _cfg([synth.BlockShape(256, 4, 8192)], max_tokens=1 << 20, arena=256, arena_bytes=1 << 40)
     assert _create_status(cfg)[0] == L.E_INVAL
     assert "4 GiB" in L.lib().dlo_last_error().decode()
+    # the q,k projection output is tokens x 2 d_model: with d_mlp = d_model it
+    # is the widest operand (200000 x 8192 x 2 bytes fits, x 2 does not)
+    cfg, keep = _cfg([synth.BlockShape(8192, 64, 8192)], max_tokens=200000, arena=256, arena_bytes=1 << 40)
+    assert _create_status(cfg)[0] == L.E_INVAL
+    assert "4 GiB" in L.lib().dlo_last_error().decode()
 
 
 def test_abi_version_and_mixed_cond_rejected():
