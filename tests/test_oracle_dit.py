@@ -99,6 +99,24 @@ def _attn_loops(q, k, v, heads):
     return out
 
 
+def test_modulate_special_cases_and_feature_broadcast():
+    """adaLN modulation h (1 + scale) + shift acts per feature: zero scale
+    and shift leave h unchanged, scale -1 leaves only the shift, and on a
+    non-square input each feature column gets its own pair (a row-wise
+    broadcast or a swapped shift/scale fails the element loop)."""
+    rng = np.random.default_rng(3)
+    h = rng.standard_normal((5, 3))
+    z = np.zeros(3)
+    assert np.array_equal(D.modulate(h, z, z), h)
+    shift = rng.standard_normal(3)
+    assert np.array_equal(D.modulate(h, shift, -np.ones(3)), np.broadcast_to(shift, h.shape))
+    scale = rng.standard_normal(3)
+    got = D.modulate(h, shift, scale)
+    for t in range(5):
+        for j in range(3):
+            assert got[t, j] == h[t, j] * (1.0 + scale[j]) + shift[j]
+
+
 def test_attention_bruteforce_tiny():
     rng = np.random.default_rng(5)
     for tq, tk in ((1, 1), (3, 5), (8, 8)):
