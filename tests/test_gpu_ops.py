@@ -239,12 +239,12 @@ def test_gemm_large_tile_shapes():
                                          (dlo.EPI_GATED_F32, 8192 + 17, 8192 - 48, 512),
                                          (dlo.EPI_VT_F16, 8192 + 128, 8192 - 64, 512)])
 def test_gemm_long_k_and_ragged_large_tiles(epi, M, N, K):
-    """The 256x128 tile (K >= 4096, the MLP-down shape class, and the
-    transposed v projection of a d = 4096 block at T <= 2048), the 256x256
-    tile and the one-wave-per-SIMD 256x256 tile (1024 tiles and more), with a
-    ragged last tile row and column, every epilogue, checked on sampled rows
-    (every row of the last, partial tile row included) against fp64
-    products."""
+    """The 256x128 tile (K >= 4096 with fewer than 256 tiles of 256x256: the
+    MLP-down shape class, and the transposed v projection of a d = 4096 block
+    at T <= 2048) and the one-wave-per-SIMD 256x256 tile (256 tiles and
+    more), with a ragged last tile row and column, every epilogue, checked on
+    sampled rows (every row of the last, partial tile row included) against
+    fp64 products."""
     rng = np.random.default_rng(M + N + K + epi)
     vt = epi == dlo.EPI_VT_F16
     w_rows = N - 77 if vt else N  # transposed v: columns past the last token repeat it
