@@ -467,10 +467,15 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
   const int xcd = bid & 7, local = bid >> 3;
   const int per = nb >> 3, rem = nb & 7;
   const int logical = (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
-  const int group_span = kGroupM * tiles_n;
+  // groups of 8 tile rows for long-K products over 32 or more tile columns
+  // (warm, same box: MLP down of the large block 8192x8192x32768 3782 ->
+  // 3597 us, 8192x8192x16384 1820 -> 1789 us; shorter K or fewer columns
+  // measured level or up to 2.5% slower with 8)
+  const int group_m = (g.K >= 16384 && tiles_n >= 32) ? 8 : kGroupM;
+  const int group_span = group_m * tiles_n;
   const int group = logical / group_span;
-  const int first_m = group * kGroupM;
-  const int gsz = min(tiles_m - first_m, kGroupM);
+  const int first_m = group * group_m;
+  const int gsz = min(tiles_m - first_m, group_m);
   const int in_group = logical - group * group_span;
   const int tile_m = first_m + in_group % gsz;
   const int tile_n = in_group / gsz;
