@@ -387,6 +387,11 @@ def main():
              "slowest": [[(r["forward"] - f_first) // (len(Ts) * max(repeats, 1)), r["block"],
                           round(r["end"] - r["start"], 4)]
                          for r in sorted(rs, key=lambda r: r["start"] - r["end"])[:4]]}
+        # average launch per timed step (a slow stretch shows as one step)
+        per_step = {}
+        for r in rs:
+            per_step.setdefault((r["forward"] - f_first) // (len(Ts) * max(repeats, 1)), []).append(r["end"] - r["start"])
+        e["avg_ms_by_step"] = [round(sum(v) / len(v), 4) for _, v in sorted(per_step.items())]
         if unit == "flop":
             e["TFLOPs"] = work / (avg * 1e-3) / 1e12
             e["mfma_frac"] = e["TFLOPs"] / PEAK_BF16_TFLOPS
