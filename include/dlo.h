@@ -129,7 +129,7 @@ typedef struct dlo_config {
   int32_t max_tokens;          /* largest token count dlo_forward accepts, in [1, 2^20], and
                                   max_tokens * max(2 * d_model, d_mlp) * 2 bytes below 4 GiB */
   int64_t landing_chunk_elems; /* largest H2D chunk in elements; 0 = default
-                                  min(S_max, ceil(dp * S_max / 4), 2^26) with
+                                  min(S_max, ceil(dp * S_max / 4), 2^27) with
                                   S_max the largest shard (the two landing
                                   buffers then hold at most half of the
                                   largest block); else >= 4096.

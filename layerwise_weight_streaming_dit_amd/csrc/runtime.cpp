@@ -55,15 +55,17 @@ namespace {
 
 constexpr size_t kAlign = 256;
 // Default H2D chunk: min(largest shard, a quarter of the largest padded block,
-// 2^26 elements = 128 MiB).  The two landing buffers then add at most half a
-// block, and at most 256 MiB, to the two slots' weight bytes: slots + landing
-// <= 2.5 x the largest block at any dp.  Transfers of 128 MiB keep the host
-// link busier than 32 MiB ones while the compute stream holds every CU (each
-// transfer's reconstruction waits for CUs to free up, and the next transfer
-// into that landing buffer waits for the reconstruction): 8 blocks of the
-// d 8192 workload stream in 241.7 ms with 128 MiB transfers, 256.1 ms with
+// 2^27 elements = 256 MiB).  The two landing buffers then add at most half a
+// block, and at most 512 MiB, to the two slots' weight bytes: slots + landing
+// <= 2.5 x the largest block at any dp.  Larger transfers keep the host link
+// busier, since each copy carries a fixed set-up cost and each transfer's
+// landing buffer is refilled only after its reconstruction, which waits for
+// CUs the GEMMs hold: the 80-block d 8192 step streams at 33.5-33.7 blocks/s
+// with 128 MiB transfers, 34.2-34.3 with 256 MiB and 33.9-34.0 with quarter
+// blocks (409 MB, whose longer first transfer delays each block's compute);
+// 8 of those blocks took 241.7 ms with 128 MiB transfers and 256.1 ms with
 // 32 MiB ones.
-constexpr int64_t kDefaultChunk = int64_t(1) << 26;
+constexpr int64_t kDefaultChunk = int64_t(1) << 27;
 constexpr int64_t kMinChunk = 4096;
 constexpr int kLandSlack = 8;  // landing offset (elements) used to co-align with the slot
 constexpr size_t kMaxTraceEvents = size_t(1) << 20;  // bound on recorded trace events per context

@@ -58,11 +58,11 @@ def test_required_bytes_two_slots_of_largest_block(name):
         one_slot_aligned = -(-one_slot // 256) * 256
         assert sz["slots"] == 2 * one_slot_aligned
         assert sz["total"] >= sz["slots"] + sz["landing"] + sz["workspace"]
-        # landing: two chunks of at most min(S_max, a quarter block, 2^26)
+        # landing: two chunks of at most min(S_max, a quarter block, 2^27)
         # elements (+ co-alignment slack), so that every byte that ever holds
         # weights -- slots and landing buffers -- is at most 2.5 blocks
         s_max = max(OS.shard_size(n, dp) for n in numels)
-        chunk = min(s_max, -(-dp * s_max // 4), 1 << 26)
+        chunk = min(s_max, -(-dp * s_max // 4), 1 << 27)
         assert sz["landing"] <= 2 * (-(-(chunk + 8) * 2 // 256) * 256)
         max_block = 2 * dp * s_max
         # (+ 256-byte alignment of each of the four buffers and the landing
