@@ -347,6 +347,55 @@ def test_next_forward_first_block_streams_under_last_block(L):
     assert np.array_equal(got, _chain(ref, x, cond, 3))
 
 
+def _overlap(a, b):
+    """Length of the intersection of interval a with the union of intervals b."""
+    segs = sorted((max(a["start"], r["start"]), min(a["end"], r["end"])) for r in b
+                  if r["end"] > a["start"] and r["start"] < a["end"])
+    tot, cs, ce = 0.0, None, None
+    for s, e in segs:
+        if ce is None or s > ce:
+            tot += (ce - cs) if ce is not None else 0.0
+            cs, ce = s, e
+        else:
+            ce = max(ce, e)
+    return tot + ((ce - cs) if ce is not None else 0.0)
+
+
+def test_h2d_hidden_behind_compute_when_compute_bound():
+    """The method's overlap target on the compute-bound mid-video block
+    (d 5120, 40 heads, MLP 20480, T 16384: ~15 ms of kernels against ~12 ms
+    of H2D per block): the copies of blocks 1..L-1 run while earlier blocks
+    compute, so at least 90% of their H2D time is hidden behind compute, and
+    the forward takes within 10% of its summed compute plus the first
+    block's staging."""
+    L, T = 3, 16384
+    shp = synth.workload("midvideo").blocks[0]
+    ctx = _ctx([shp] * L, 4, T, flags=dlo.FLAG_TRACE)
+    numels = [OL.block_numel(shp)] * L
+    for b, flat in synth.iter_block_weights(3, numels, threads=8):
+        ctx.load_shards(b, flat)
+    x, cond = synth.activations(T, shp.d_model), synth.conditioning(256)
+    _run(ctx, x, cond)  # first forward: warm-up
+    ctx.trace()
+    _run(ctx, x, cond)
+    tr = ctx.trace()
+    comp = [r for r in tr if r["kind"] == "compute"]
+    h2d = [r for r in tr if r["kind"] == "h2d" and r["block"] >= 1]
+    assert len(comp) == L and h2d
+    h2d_time = sum(r["end"] - r["start"] for r in h2d)
+    hidden = sum(_overlap(r, comp) for r in h2d)
+    assert hidden >= 0.9 * h2d_time, (hidden, h2d_time)
+    c = sum(r["end"] - r["start"] for r in comp)
+    all_h2d = [r for r in tr if r["kind"] == "h2d"]
+    busy_h2d = _overlap({"start": min(r["start"] for r in all_h2d), "end": max(r["end"] for r in all_h2d)}, all_h2d)
+    assert c > busy_h2d, (c, busy_h2d)  # compute-bound, as designed
+    stage0 = max(r["end"] for r in tr if r["kind"] == "asm" and r["block"] == 0) - \
+        min(r["start"] for r in tr if r["kind"] == "h2d" and r["block"] == 0)
+    t_fwd = max(r["end"] for r in comp) - min(r["start"] for r in tr)
+    assert t_fwd <= 1.1 * (c + stage0), (t_fwd, c, stage0)
+    ctx.close()
+
+
 def test_forwards_on_alternating_streams_match_one_stream():
     # consecutive calls may pass different streams; each call is ordered after
     # the previous one (the context's workspace and x are shared)
