@@ -535,7 +535,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp16",
-        "precision": "weights bf16 (streamed, reconstructed bit-exact, widened to fp16 in registers); "
+        "precision": "weights bf16 as streamed, converted to fp16 by the reconstruction (exact for |w| >= 2^-17); "
                      "fp16 matrix-core operands; fp32 accumulation, softmax, residual and modulation",
         "data": "synthetic (seeded N(0,0.02) bf16 weights, N(0,1) activations)",
         "config": {"workload": wl.description + (f"; first {L} of {wl.num_blocks} blocks streamed"

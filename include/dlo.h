@@ -32,7 +32,7 @@
  *   - a context is not thread-safe; calls on one context must not overlap.
  *
  * Data formats:
- *   - bf16 values travel as their 16-bit patterns (uint16_t);
+ *   - bf16 and fp16 values travel as their 16-bit patterns (uint16_t);
  *   - a block's flat weight is the dense concatenation, in this order, of
  *       Wqkv[3d][d] bqkv[3d] Wo[d][d] bo[d] W1[m][d] b1[m] W2[d][m] b2[d]
  *       Wada[6d][c] bada[6d] extra_0[..] extra_1[..] ...
@@ -49,10 +49,11 @@
  * LayerNorm has no affine parameters and eps 1e-6; attention is non-causal
  * multi-head softmax(q k^T / sqrt(d / heads)) v.  Between blocks of different
  * width the residual keeps its first min(d_in, d_out) features and zero-fills
- * the rest.  Weights stay the streamed bf16 values, widened to fp16 in
- * registers for the matrix cores (exact for |w| >= 2^-17; smaller magnitudes
- * round to fp16's subnormal grid, error <= 2^-25; |w| > 65504 overflows);
- * biases and the adaLN weights are read as bf16 in fp32 arithmetic;
+ * the rest.  Weights are streamed as bf16; the reconstruction writes the
+ * gathered layer into its slot as fp16, the matrix cores' operand type (exact
+ * for |w| >= 2^-17; smaller magnitudes round to fp16's subnormal grid, error
+ * <= 2^-25; |w| > 65504 overflows), and every kernel of the block reads the
+ * parameters in that form (biases and the adaLN weights in fp32 arithmetic);
  * activations between kernels are fp16; matrix-core accumulation, softmax,
  * the residual x and the modulation vectors are fp32.
  */
@@ -87,7 +88,7 @@ typedef int32_t dlo_status;
 #define DLO_FLAG_SERIALIZE 0x2u    /* test hook: synchronous schedule (copy,
                                       wait, reconstruct, wait, compute), same
                                       kernels */
-#define DLO_FLAG_POISON_SLOTS 0x4u /* test hook: fill a slot with bf16 NaN
+#define DLO_FLAG_POISON_SLOTS 0x4u /* test hook: fill a slot with fp16 NaN
                                       before reconstructing into it, so a read
                                       ahead of the reconstruction shows up */
 #define DLO_FLAG_TRACE_KERNELS 0x8u /* record only the compute-stream intervals
@@ -337,7 +338,8 @@ DLO_API dlo_status dlo_get_shard(dlo_ctx* ctx, int32_t block, int32_t rank,
 
 /* Run the real H2D -> landing -> reconstruction path for one block into
  * slot (block % 2), synchronously, and copy the reconstructed numel elements
- * to host_out (capacity cap elements).  Must not overlap a forward. */
+ * (fp16 patterns: the flat weight converted element by element) to host_out
+ * (capacity cap elements).  Must not overlap a forward. */
 DLO_API dlo_status dlo_debug_assemble(dlo_ctx* ctx, int32_t block, uint16_t* host_out,
                                       int64_t cap);
 

@@ -4,11 +4,13 @@
  * Each call launches exactly the kernel dlo_forward launches for that step,
  * on the caller's stream, without a context.  They exist so each step can be
  * checked against the oracle and timed on its own.  All pointers are device
- * pointers; bf16 and fp16 values are their 16-bit patterns.  Weights are
- * bf16 (as streamed); activations between kernels are fp16 (fp16 has three
- * more mantissa bits than bf16 and runs the matrix cores at the same rate;
- * with bf16 activations the rounding error of the widest block reaches the
- * 2e-2 output tolerance).  Calls are asynchronous
+ * pointers; bf16 and fp16 values are their 16-bit patterns.  Weights arrive
+ * as bf16 (as streamed) and dlo_op_assemble converts them to fp16 while
+ * reconstructing, so the other calls take fp16 weights and biases, as the
+ * forward's kernels read them from the slot; activations between kernels are
+ * fp16 (fp16 has three more mantissa bits than bf16 and runs the matrix cores
+ * at the same rate; with bf16 activations the rounding error of the widest
+ * block reaches the 2e-2 output tolerance).  Calls are asynchronous
  * with respect to the host.  Shapes are validated on the host before any
  * launch (DLO_E_INVAL / DLO_E_SHAPE, nothing enqueued); a failed launch
  * returns DLO_E_HIP.  Error messages come from dlo_last_error().
@@ -24,16 +26,18 @@ extern "C" {
 
 /* Reconstruction (the single-GPU stand-in for all_gather_into_tensor,
  * release page section "Weight sharding with AllGather reconstruction"):
- * dst[i] = src[i] for i in [0, n).  Any 2-byte alignment is accepted; when
- * dst and src have the same address modulo 16 bytes the kernel copies in
- * 16-byte vectors with a scalar head and tail, which is how dlo_forward
- * lands every chunk.  The ranges must not overlap. */
+ * dst[i] = fp16(src[i]) for the bf16 values src[i], i in [0, n), rounded to
+ * nearest even (exact for |src[i]| >= 2^-17; rounded to fp16's subnormal grid
+ * below, error <= 2^-25; inf above 65504).  Any 2-byte alignment is
+ * accepted; when dst and src have the same address modulo 16 bytes the kernel
+ * works in 16-byte vectors with a scalar head and tail, which is how
+ * dlo_forward lands every chunk.  The ranges must not overlap. */
 DLO_API dlo_status dlo_op_assemble(uint16_t* dst, const uint16_t* src, int64_t n,
                                    hipStream_t stream);
 
 /* adaLN modulation (DiT adaLN-Zero conditioning):
  * mod[r] = sum_j w[r][j] * silu(cond[j]) + b[r] for r in [0, rows), fp32
- * accumulation.  w: bf16 [rows][c] row-major; b: bf16 [rows]; cond, mod: fp32.
+ * accumulation.  w: fp16 [rows][c] row-major; b: fp16 [rows]; cond, mod: fp32.
  * c must be a multiple of 64 and at most 4096. */
 DLO_API dlo_status dlo_op_adaln(const uint16_t* w, const uint16_t* b, const float* cond,
                                 float* mod, int32_t rows, int32_t c, hipStream_t stream);
@@ -50,9 +54,8 @@ DLO_API dlo_status dlo_op_ln_modulate(const float* xin, int32_t d_in, float* xou
                                       int32_t tokens, int32_t d, hipStream_t stream);
 
 /* GEMM on MFMA: acc[i][j] = sum_k a[i][k] * w[j][k] for i in [0, M), j in
- * [0, N), fp32 accumulation.  One operand is a weight matrix (bf16, widened to
- * fp16 in registers: exact for |w| >= 2^-17, rounded to fp16's subnormal grid
- * below, overflowing above 65504), the other fp16 activations: for DLO_EPI_VT_F16 `a` is
+ * [0, N), fp32 accumulation.  Both operands are fp16: one is a weight matrix
+ * (as dlo_op_assemble writes it), the other activations: for DLO_EPI_VT_F16 `a` is
  * the weight and `w` the activation, for every other epilogue `a` is the
  * activation and `w` the weight.  Rows of w at or past w_rows are read as row
  * w_rows - 1 (so padded output columns stay finite).  Epilogues (fp16
@@ -62,7 +65,7 @@ DLO_API dlo_status dlo_op_ln_modulate(const float* xin, int32_t d_in, float* xou
  *   DLO_EPI_GATED_F32      out fp32 [M][ldo]:  out[i][j] += gate[j] * (acc + bias[j])
  *   DLO_EPI_VT_F16         out fp16 [M][ldo]:  out[i][p(j)] = acc + bias[i]
  * where p(j) swaps bits 2 and 3 of j (the transposed v layout attention
- * reads, see dlo_op_attention).  bias is bf16, gate fp32.  M >= 1; N a
+ * reads, see dlo_op_attention).  bias is fp16, gate fp32.  M >= 1; N a
  * multiple of 16; K a multiple of 128; lda, ldw multiples of 8 and >= K;
  * ldo >= N and a multiple of 8 (of 4 for the fp32 epilogue), so that every
  * output row starts 16-byte aligned; 1 <= w_rows <= N; a, w and out 16-byte

@@ -8,7 +8,6 @@
 
 namespace dlo {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -29,19 +28,31 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Eight bf16 weights -> eight fp16 operands for the fp16 matrix cores.  A bf16
-// value has 8 significant bits and fp16 has 11.  Magnitudes in [2^-14, 65504]
-// are fp16 normals and widen exactly; in [2^-17, 2^-14) they become fp16
-// subnormals (spacing 2^-24), which still hold all 8 bits of a bf16 value
-// there, so they widen exactly too; below 2^-17 they round to the subnormal
-// grid (absolute error <= 2^-25); above 65504 they overflow.
-__device__ __forceinline__ f16x8_t bf16x8_to_f16x8(bf16x8_t v) {
-  const u32x4_t w = __builtin_bit_cast(u32x4_t, v);
-  u32x4_t o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    o[i] = pack_f16x2(__uint_as_float(w[i] << 16), __uint_as_float(w[i] & 0xffff0000u));
-  return __builtin_bit_cast(f16x8_t, o);
+// bf16 -> fp16, two at a time (bits 0..15 and 16..31 of w), round to
+// nearest even.  A bf16 value has 8 significant bits and fp16 has 11.
+// Magnitudes in [2^-14, 65504] are fp16 normals and convert exactly; in
+// [2^-17, 2^-14) they become fp16 subnormals (spacing 2^-24), which still
+// hold all 8 bits of a bf16 value there, so they convert exactly too; below
+// 2^-17 they round to the subnormal grid (absolute error <= 2^-25); above
+// 65504 they overflow.  The reconstruction writes the gathered layer through
+// this, so the weights reach the matrix cores as fp16.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack_f16x2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+
+// fp16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// Four fp16 (two dwords, lowest element first) -> fp32 (exact).  The dwords
+// are copied out of the vector before the bit casts: a bit cast applied to a
+// vector element expression (b.y) has been compiled as a cast of element 0.
+__device__ __forceinline__ f32x4_t f16x4_to_f32x4(u32x2_t b) {
+  const uint32_t b0 = b.x, b1 = b.y;
+  const f16x2_t lo = __builtin_bit_cast(f16x2_t, b0), hi = __builtin_bit_cast(f16x2_t, b1);
+  return f32x4_t{static_cast<float>(lo[0]), static_cast<float>(lo[1]), static_cast<float>(hi[0]),
+                 static_cast<float>(hi[1])};
 }
 
 // Column position of token j in the transposed v buffer: inside every aligned

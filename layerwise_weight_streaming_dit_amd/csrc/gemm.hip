@@ -21,12 +21,12 @@
 // each XCD a contiguous range of tiles, walked in groups of kGroupM tile rows,
 // so tiles that share A rows or W rows share an L2.
 //
-// Precision: weights are the streamed bf16 values, widened to fp16 in
-// registers (exact for |w| >= 2^-17; smaller magnitudes round to fp16's
-// subnormal grid, |w| > 65504 would overflow); activations are fp16;
-// accumulation is fp32.  (fp16 operands have 3 more mantissa bits than bf16
-// at the same matrix-core rate; with bf16 activations the rounding error of a
-// d = 8192 block reaches the 2e-2 output tolerance.)
+// Precision: both operands and the biases are fp16 -- the weights are the
+// streamed bf16 values as the reconstruction converted them (exact for
+// |w| >= 2^-17; smaller magnitudes round to fp16's subnormal grid, |w| > 65504
+// would overflow) -- and accumulation is fp32.  (fp16 operands have 3 more
+// mantissa bits than bf16 at the same matrix-core rate; with bf16 activations
+// the rounding error of a d = 8192 block reaches the 2e-2 output tolerance.)
 //
 // Epilogues fuse the DiT block's elementwise work into the GEMM:
 //   bias -> fp16 (q/k projection), bias + GELU(tanh) -> fp16 (MLP up),
@@ -67,10 +67,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
   constexpr int STAGE_A = BM * kBK, STAGE_B = BN * kBK;  // elements per stage
   constexpr int LA = BM / 8 / W, LB = BN / 8 / W;        // 1 KB DMA loads per wave per stage
   static_assert(LA * 8 * W == BM && LB * 8 * W == BN, "tile/waves mismatch");
-  // The transposed v projection multiplies weights (A) by activations (W);
-  // every other projection multiplies activations (A) by weights (W).
-  constexpr bool A_IS_WEIGHT = EPI == EPI_VT_F16;
-
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[STAGE_A];
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[STAGE_A];
   __shared__ __attribute__((aligned(1024))) uint16_t sB0[STAGE_B];
@@ -176,38 +172,29 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
       for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
 
   // Fragments of one 16-wide k slice of a stage.
-  auto read_frags = [&](auto S, int ks, bf16x8_t (&fa)[TM], bf16x8_t (&fb)[TN]) {
+  auto read_frags = [&](auto S, int ks, f16x8_t (&fa)[TM], f16x8_t (&fb)[TN]) {
     const uint16_t* a = stageA(S);
     const uint16_t* b = stageB(S);
     const int c = ks * 2 + (lane >> 5);
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
       const int row = wm * WTM + tm * 32 + (lane & 31);
-      fa[tm] = *reinterpret_cast<const bf16x8_t*>(a + row * kBK + ((c ^ swz(row)) << 3));
+      fa[tm] = *reinterpret_cast<const f16x8_t*>(a + row * kBK + ((c ^ swz(row)) << 3));
     }
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
       const int row = wn * WTN + tn * 32 + (lane & 31);
-      fb[tn] = *reinterpret_cast<const bf16x8_t*>(b + row * kBK + ((c ^ swz(row)) << 3));
+      fb[tn] = *reinterpret_cast<const f16x8_t*>(b + row * kBK + ((c ^ swz(row)) << 3));
     }
   };
-  // The weight operand (bf16) is widened to fp16 in registers, once per
-  // fragment; the activation operand is already fp16.
   // `after_row(tm)` runs after the MFMAs of tile row tm (used to interleave
   // the next step's DMA loads with the matrix work).
-  auto mfmas = [&](const bf16x8_t (&fa)[TM], const bf16x8_t (&fb)[TN], auto&& after_row) {
-    f16x8_t a16[TM], b16[TN];
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-      a16[tm] = A_IS_WEIGHT ? bf16x8_to_f16x8(fa[tm]) : __builtin_bit_cast(f16x8_t, fa[tm]);
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-      b16[tn] = A_IS_WEIGHT ? __builtin_bit_cast(f16x8_t, fb[tn]) : bf16x8_to_f16x8(fb[tn]);
+  auto mfmas = [&](const f16x8_t (&fa)[TM], const f16x8_t (&fb)[TN], auto&& after_row) {
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b16[tn], a16[tm], acc[tm][tn], 0, 0, 0);
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[tn], fa[tm], acc[tm][tn], 0, 0, 0);
       after_row(tm);
     }
   };
@@ -221,7 +208,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
   // its first use; the explicit lgkmcnt(0) before each batch of reads retires
   // the previous batch, so no wait lands between reads and the MFMAs they
   // overlap.
-  bf16x8_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+  f16x8_t fa0[TM], fb0[TN], fa1[TM], fb1[TN];
   // The next step's LA + LB DMA loads are spread over the tile rows of the
   // first two k slices (kPer after each row), so no wave stalls on a full
   // address queue while it has MFMAs to issue.
@@ -321,15 +308,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
               // transposed v: per-row bias; tokens c..c+3 land at their
               // permuted key positions, consecutive too (the tile's first
               // column is a multiple of 16, and only bits 2 and 3 move)
-              const float rb = bf16_to_f32(g.bias[min(m0 + wm * WTM + tm * 32 + (lane & 31), g.M - 1)]);
+              const float rb = f16_to_f32(g.bias[min(m0 + wm * WTM + tm * 32 + (lane & 31), g.M - 1)]);
               v += rb;
               c = vt_key_position(c);
             } else {
               const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(g.bias + min(col[tn][q], g.N - 4));
-              v.x += __uint_as_float(bb.x << 16);
-              v.y += __uint_as_float(bb.x & 0xffff0000u);
-              v.z += __uint_as_float(bb.y << 16);
-              v.w += __uint_as_float(bb.y & 0xffff0000u);
+              v += f16x4_to_f32x4(bb);
             }
             if constexpr (EPI == EPI_BIAS_GELU_F16) {
               v.x = gelu_tanh(v.x);
@@ -371,11 +355,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(g.bias + min(col[tn][q], g.N - 4));
+          const f32x4_t bf = f16x4_to_f32x4(bb);
           f32x4_t v;
-          v.x = acc[tm][tn][4 * q] + __uint_as_float(bb.x << 16);
-          v.y = acc[tm][tn][4 * q + 1] + __uint_as_float(bb.x & 0xffff0000u);
-          v.z = acc[tm][tn][4 * q + 2] + __uint_as_float(bb.y << 16);
-          v.w = acc[tm][tn][4 * q + 3] + __uint_as_float(bb.y & 0xffff0000u);
+          v.x = acc[tm][tn][4 * q] + bf.x;
+          v.y = acc[tm][tn][4 * q + 1] + bf.y;
+          v.z = acc[tm][tn][4 * q + 2] + bf.z;
+          v.w = acc[tm][tn][4 * q + 3] + bf.w;
           *reinterpret_cast<f32x4_t*>(region + (lane & 31) * RS + tn * 32 + 8 * q + 4 * (lane >> 5)) = v;
         }
       const int c4 = (lane & 15) * 4, cc = n0 + wn * WTN + c4;
@@ -414,19 +399,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------
 // 256x256 tile with ONE wave per SIMD (four waves).  The waves split the
 // tile along the dimension of the activation operand, so each wave owns its
-// own slice of the weight operand and widens every weight fragment it uses
-// exactly once per k slice (no two waves widen the same weights):
+// own slice of the weight operand (no two waves read the same weight
+// fragments):
 //   WM=1, WN=4: waves own 64 weight rows (columns of C), 256x64 per wave;
 //   WM=4, WN=1: the transposed v projection (weights are the A operand),
 //               waves own 64 weight rows, 64x256 per wave.
 // Per 64-wide K step a wave issues 64 MFMAs (256 fp32 accumulators per lane
-// in the accumulation registers) against 40 fragment reads, and widens 8
-// weight fragments.  With no second wave on the SIMD the stream is
-// pipelined by hand:
+// in the accumulation registers) against 40 fragment reads.  With no second
+// wave on the SIMD the stream is pipelined by hand:
 //   * the fragments of k slice j+1 are read one after each of slice j's
-//     first ten MFMAs, and the weight fragments among them (read first) are
-//     widened to fp16 a few MFMAs later, between MFMAs, so no MFMA waits for
-//     a conversion; the stage loads are buffer loads (dma16_buf), so the
+//     first ten MFMAs; the stage loads are buffer loads (dma16_buf), so the
 //     compiler's waits for the reads are exact and each MFMA of the next
 //     slice waits only for its own fragments;
 //   * the step's barrier sits before the last slice's MFMAs: every wave has
@@ -524,11 +506,9 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[tm][tn][r] = 0.f;
 
-  // Fragment pipeline: raw fragments double-buffered by slice parity
-  // (four slices per step: parities 0, 1, 0, 1); wc holds the widened
-  // weight fragments.
-  bf16x8_t ra[2][TM], rb[2][TN];
-  f16x8_t wc[2][NWF];
+  // Fragment pipeline: fragments double-buffered by slice parity (four
+  // slices per step: parities 0, 1, 0, 1).
+  f16x8_t ra[2][TM], rb[2][TN];
   // Fragment addresses.  Tile rows are 32 apart, so within a wave's rows
   // (which start at a multiple of 32) the chunk swizzle of fragment row
   // R + (lane % 32) is swz(lane % 32) ^ 4 for odd tiles and swz(lane % 32) for
@@ -550,14 +530,14 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
     auto rd_a = [&] {
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm)
-        ra[p][tm] = *reinterpret_cast<const bf16x8_t*>(a + tm * 32 * kBK + fo[ks][tm & 1]);
+        ra[p][tm] = *reinterpret_cast<const f16x8_t*>(a + tm * 32 * kBK + fo[ks][tm & 1]);
     };
     auto rd_b = [&] {
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
-        rb[p][tn] = *reinterpret_cast<const bf16x8_t*>(b + tn * 32 * kBK + fo[ks][tn & 1]);
+        rb[p][tn] = *reinterpret_cast<const f16x8_t*>(b + tn * 32 * kBK + fo[ks][tn & 1]);
     };
-    // the weight fragments first: their widening waits only for them
+    // the weight fragments first, in the order the MFMAs use them
     if constexpr (A_IS_WEIGHT) {
       rd_a();
       rd_b();
@@ -575,40 +555,24 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
     const bool wfrag = j < NW;
     const int t = wfrag ? j : j - NW;
     if (A_IS_WEIGHT == wfrag)
-      ra[p][t] = *reinterpret_cast<const bf16x8_t*>(stageA(S) + arow0 + t * 32 * kBK + fo[ks][t & 1]);
+      ra[p][t] = *reinterpret_cast<const f16x8_t*>(stageA(S) + arow0 + t * 32 * kBK + fo[ks][t & 1]);
     else
-      rb[p][t] = *reinterpret_cast<const bf16x8_t*>(stageB(S) + brow0 + t * 32 * kBK + fo[ks][t & 1]);
-  };
-  // widen dword q (0..3) of weight fragment f of parity P
-  auto widen_part = [&](auto P, int f, int q) {
-    constexpr int p = decltype(P)::value;
-    const u32x4_t w = __builtin_bit_cast(u32x4_t, A_IS_WEIGHT ? ra[p][f] : rb[p][f]);
-    u32x4_t o = __builtin_bit_cast(u32x4_t, wc[p][f]);
-    o[q] = pack_f16x2(__uint_as_float(w[q] << 16), __uint_as_float(w[q] & 0xffff0000u));
-    wc[p][f] = __builtin_bit_cast(f16x8_t, o);
+      rb[p][t] = *reinterpret_cast<const f16x8_t*>(stageB(S) + brow0 + t * 32 * kBK + fo[ks][t & 1]);
   };
   // The 16 MFMAs of the slice of parity P; after MFMA i, rd(i) (fragment
-  // read i of the next slice, into parity P ^ 1), dma(i) and, for i = 4, 6,
-  // ..., 14, a quarter of a weight fragment of parity P ^ 1 (read after MFMAs
-  // 0 and 1).  The compiler's LDS waits are exact (see dma16_buf): each MFMA
-  // waits only for its own fragments.
+  // read i of the next slice, into parity P ^ 1) and dma(i).  The compiler's
+  // LDS waits are exact (see dma16_buf): each MFMA waits only for its own
+  // fragments.
   auto mfma_slice = [&](auto P, auto&& dma, auto&& rd) {
     constexpr int p = decltype(P)::value;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      // weight fragment outer, so each widened fragment is done with early
+      // weight fragment outer: each weight fragment is done with early
       const int wf = i / (16 / NWF), af = i % (16 / NWF);
       const int tm = A_IS_WEIGHT ? wf : af, tn = A_IS_WEIGHT ? af : wf;
-      const f16x8_t a16 = A_IS_WEIGHT ? wc[p][tm] : __builtin_bit_cast(f16x8_t, ra[p][tm]);
-      const f16x8_t b16 = A_IS_WEIGHT ? __builtin_bit_cast(f16x8_t, rb[p][tn]) : wc[p][tn];
-      acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b16, a16, acc[tm][tn], 0, 0, 0);
+      acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rb[p][tn], ra[p][tm], acc[tm][tn], 0, 0, 0);
       rd(i);
       dma(i);
-      if (i >= 4 && (i & 1) == 0) {
-        const int j = (i - 4) / 2;  // 0..5: eight quarter fragments
-        widen_part(IC<p ^ 1>{}, j < 4 ? 0 : 1, j & 3);
-        if (j >= 4) widen_part(IC<p ^ 1>{}, 1, (j & 3) + 2);
-      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -630,8 +594,8 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
     mfma_slice(IC<0>{}, dma_range(IC<s ^ 1>{}, kt + 1, NEARLY, ND - NEARLY), reads(S, 1, IC<1>{}));
     mfma_slice(IC<1>{}, none, reads(S, 2, IC<0>{}));
     mfma_slice(IC<0>{}, none, reads(S, 3, IC<1>{}));
-    // step kt+1's loads have landed and slice 3 is in registers and widened:
-    // publish the next stage, release this one
+    // step kt+1's loads have landed and slice 3 is in registers: publish the
+    // next stage, release this one
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
@@ -647,10 +611,6 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
 #pragma unroll
   for (int d = 0; d < NEARLY; ++d) issue_one(IC<1>{}, 1, d);
   wait_lgkmcnt0();
-#pragma unroll
-  for (int f = 0; f < NWF; ++f)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) widen_part(IC<0>{}, f, q);
   // K is a multiple of two steps (128), so the ring unrolls without early exits
   for (int kt = 0; kt < nk; kt += 2) {
     step(IC<0>{}, kt);
@@ -683,11 +643,12 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
         for (int q = 0; q < 4; ++q) {
           const int c = tn * 32 + 8 * q + 4 * (lane >> 5);
           const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(g.bias + min(col0 + c, g.N - 4));
+          const f32x4_t bf = f16x4_to_f32x4(bb);
           f32x4_t v;
-          v.x = acc[tm][tn][4 * q] + __uint_as_float(bb.x << 16);
-          v.y = acc[tm][tn][4 * q + 1] + __uint_as_float(bb.x & 0xffff0000u);
-          v.z = acc[tm][tn][4 * q + 2] + __uint_as_float(bb.y << 16);
-          v.w = acc[tm][tn][4 * q + 3] + __uint_as_float(bb.y & 0xffff0000u);
+          v.x = acc[tm][tn][4 * q] + bf.x;
+          v.y = acc[tm][tn][4 * q + 1] + bf.y;
+          v.z = acc[tm][tn][4 * q + 2] + bf.z;
+          v.w = acc[tm][tn][4 * q + 3] + bf.w;
           *reinterpret_cast<f32x4_t*>(fr + (lane & 31) * RS + c) = v;
         }
       const f32x4_t gt = *reinterpret_cast<const f32x4_t*>(g.gate + min(cc, g.N - 4));
@@ -732,14 +693,11 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
             // transposed v: per-row bias; tokens c..c+3 land at their
             // permuted key positions, consecutive too (the tile's first
             // column is a multiple of 16, and only bits 2 and 3 move)
-            v += bf16_to_f32(g.bias[min(row0 + tm * 32 + (lane & 31), g.M - 1)]);
+            v += f16_to_f32(g.bias[min(row0 + tm * 32 + (lane & 31), g.M - 1)]);
             c = vt_key_position(c);
           } else {
             const u32x2_t bb = *reinterpret_cast<const u32x2_t*>(g.bias + min(col0 + c, g.N - 4));
-            v.x += __uint_as_float(bb.x << 16);
-            v.y += __uint_as_float(bb.x & 0xffff0000u);
-            v.z += __uint_as_float(bb.y << 16);
-            v.w += __uint_as_float(bb.y & 0xffff0000u);
+            v += f16x4_to_f32x4(bb);
           }
           if constexpr (EPI == EPI_BIAS_GELU_F16) {
             v.x = gelu_tanh(v.x);

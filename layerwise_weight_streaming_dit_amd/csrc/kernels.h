@@ -7,9 +7,10 @@
 
 namespace dlo {
 
-// Reconstruction of one landed chunk into its slot (all-gather stand-in).
+// Reconstruction of one landed chunk into its slot (all-gather stand-in):
+// dst[i] = fp16(src[i]) for the n bf16 values of src.
 hipError_t launch_assemble(uint16_t* dst, const uint16_t* src, int64_t n, hipStream_t s);
-// Fill n bf16 elements with a quiet-NaN pattern (slot poisoning test hook).
+// Fill n fp16 elements with a quiet-NaN pattern (slot poisoning test hook).
 hipError_t launch_fill_nan(uint16_t* dst, int64_t n, hipStream_t s);
 
 hipError_t launch_adaln(const uint16_t* w, const uint16_t* b, const float* cond, float* mod,

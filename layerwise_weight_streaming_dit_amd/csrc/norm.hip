@@ -27,7 +27,7 @@ __global__ __launch_bounds__(kNormThreads) void adaln_kernel(const uint16_t* __r
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r0 = (blockIdx.x * (kNormThreads / 64) + wave) * kAdaRowsPerWave;
   // rows past the end read the last row (in bounds) and store nothing
-  const float bias = bf16_to_f32(b[min(r0 + min(lane, kAdaRowsPerWave - 1), rows - 1)]);
+  const float bias = f16_to_f32(b[min(r0 + min(lane, kAdaRowsPerWave - 1), rows - 1)]);
   float acc[kAdaRowsPerWave];
 #pragma unroll
   for (int rr = 0; rr < kAdaRowsPerWave; ++rr) acc[rr] = 0.f;
@@ -38,9 +38,10 @@ __global__ __launch_bounds__(kNormThreads) void adaln_kernel(const uint16_t* __r
       v[rr] = *reinterpret_cast<const u32x2_t*>(w + static_cast<int64_t>(min(r0 + rr, rows - 1)) * c + j);
     const f32x4_t s4 = *reinterpret_cast<const f32x4_t*>(sc + j);
 #pragma unroll
-    for (int rr = 0; rr < kAdaRowsPerWave; ++rr)
-      acc[rr] += __uint_as_float(v[rr].x << 16) * s4.x + __uint_as_float(v[rr].x & 0xffff0000u) * s4.y +
-                 __uint_as_float(v[rr].y << 16) * s4.z + __uint_as_float(v[rr].y & 0xffff0000u) * s4.w;
+    for (int rr = 0; rr < kAdaRowsPerWave; ++rr) {
+      const f32x4_t wv = f16x4_to_f32x4(v[rr]);
+      acc[rr] += wv.x * s4.x + wv.y * s4.y + wv.z * s4.z + wv.w * s4.w;
+    }
   }
   float mine = 0.f;
 #pragma unroll

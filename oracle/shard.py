@@ -13,6 +13,11 @@ Release page, section "Weight sharding with AllGather reconstruction":
   rank order; the first total_numel elements of it are the flat weight.
 
 Pinning is a property of host memory, not of values, so it has no oracle.
+
+The GPU path keeps the reconstructed layer in its matrix cores' operand type,
+fp16 (a reading of the precision the pages leave to the hardware: fp16 has
+the bf16 rate on these matrix cores and three more mantissa bits);
+``as_f16_bits`` is that conversion, element by element.
 """
 from __future__ import annotations
 
@@ -60,3 +65,14 @@ def unshard(shards: Sequence[np.ndarray], numel: int) -> np.ndarray:
     if numel > full.shape[0]:
         raise ValueError("numel exceeds the gathered length")
     return full[:numel].copy()
+
+
+def as_f16_bits(bf16_bits: np.ndarray) -> np.ndarray:
+    """Each bf16 value (given as its 16-bit pattern) rounded to the nearest
+    fp16 value, ties to even, fp16 subnormals included, magnitudes past
+    fp16's range to infinity; returned as fp16 bit patterns.  Every bf16 value
+    of magnitude >= 2^-17 and <= 65504 is an fp16 value already and is kept
+    exactly."""
+    f = (np.ascontiguousarray(bf16_bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    with np.errstate(over="ignore"):
+        return f.astype(np.float16).view(np.uint16)

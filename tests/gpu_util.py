@@ -26,8 +26,24 @@ def host(t, dtype=None) -> np.ndarray:
     return a
 
 
-def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
-    return (np.ascontiguousarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+def f16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def assert_reconstructed(got: np.ndarray, flat_bf16: np.ndarray) -> None:
+    """The reconstructed layer (fp16 patterns) is the flat bf16 weight
+    converted element by element (oracle.shard.as_f16_bits), bit for bit; a
+    bf16 NaN may come out as any fp16 NaN."""
+    from oracle import shard as OS
+    got = np.asarray(got, np.uint16)
+    flat_bf16 = np.asarray(flat_bf16, np.uint16)
+    assert got.shape == flat_bf16.shape
+    want = OS.as_f16_bits(flat_bf16)
+    nan_in = ((flat_bf16 & 0x7F80) == 0x7F80) & ((flat_bf16 & 0x007F) != 0)
+    bad = np.flatnonzero((got != want) & ~nan_in)
+    assert bad.size == 0, (bad[:8], got[bad[:8]], want[bad[:8]])
+    g = got[nan_in]
+    assert np.all(((g & 0x7C00) == 0x7C00) & ((g & 0x03FF) != 0))
 
 
 def within(got, want, rtol=RTOL, atol=ATOL):

@@ -4,10 +4,11 @@
 // The HIP runtime is replaced by an in-order fake: "device" memory is host
 // memory, every stream executes its work at enqueue time (so the enqueue order
 // is the execution order), events carry a logical timestamp, copies are
-// memcpy.  The reconstruction launcher really copies (it is a plain copy by
-// definition); the block's compute launchers record their arguments and check,
-// at the moment they run, that the slot they read holds exactly the block's
-// gathered bf16 weights.  This exercises, on the CPU, the host logic of the
+// memcpy.  The reconstruction launcher here copies the bits unchanged (the
+// real kernel also converts each value to fp16, which the GPU tests check), so
+// the block's compute launchers, which record their arguments, can check at
+// the moment they run that the slot they read holds exactly the block's
+// gathered weights.  This exercises, on the CPU, the host logic of the
 // method's runtime (vLLM-Omni release page, sections "Weight sharding with
 // AllGather reconstruction" and "Double-buffered prefetch with H2D + AllGather
 // overlap"): shard sizing, pinned shard contents, chunking of the gather

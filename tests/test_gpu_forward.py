@@ -7,7 +7,7 @@ import pytest
 
 import synth
 from oracle import dit as D, layout as OL, shard as OS, trace as OT
-from gpu_util import dev, host, within, torch
+from gpu_util import assert_reconstructed, dev, host, within, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -46,7 +46,7 @@ def test_debug_assemble_tiny_bit_exact():
             assert np.array_equal(ctx.get_shard(b, r), ref[r])
     for b, flat in W.items():
         got = ctx.debug_assemble(b)
-        assert np.array_equal(got, OS.unshard(OS.shard(flat, 4), len(flat)))
+        assert_reconstructed(got, OS.unshard(OS.shard(flat, 4), len(flat)))
 
 
 @pytest.mark.parametrize("dp", [3, 8])
@@ -57,7 +57,7 @@ def test_debug_assemble_irregular_bit_exact(dp):
     for b in range(2):
         flat = synth.block_weights(wl.wid, b, OL.block_numel(shapes[b]))
         ctx.load_shards(b, flat)
-        assert np.array_equal(ctx.debug_assemble(b), flat)
+        assert_reconstructed(ctx.debug_assemble(b), flat)
 
 
 def test_debug_assemble_random_numel_sweep():
@@ -71,7 +71,8 @@ def test_debug_assemble_random_numel_sweep():
         ctx = _ctx([shp], dp, 16, chunk=chunk)
         flat = rng.integers(0, 1 << 16, size=n, dtype=np.uint16)
         ctx.load_shards(0, flat)
-        assert np.array_equal(ctx.debug_assemble(0), flat), (dp, extra, chunk)
+        print(f"dp {dp} extra {extra} chunk {chunk}", flush=True)
+        assert_reconstructed(ctx.debug_assemble(0), flat)
         ctx.close()
 
 
@@ -141,7 +142,7 @@ def test_smallest_block_with_all_padding_shards():
     ctx.load_shards(1, flat[::-1].copy())
     for r in (0, dp - 1):
         assert np.array_equal(ctx.get_shard(0, r), OS.shard(flat, dp)[r])
-    assert np.array_equal(ctx.debug_assemble(0), flat)
+    assert_reconstructed(ctx.debug_assemble(0), flat)
     x = synth.activations(64, 128)
     cond = synth.conditioning(64)
     got = _run(ctx, x, cond)

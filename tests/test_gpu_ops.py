@@ -4,8 +4,8 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import dit as D
-from gpu_util import dev, host, bf16_to_f64, within, torch
+from oracle import dit as D, shard as OS
+from gpu_util import assert_reconstructed, dev, host, within, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -14,6 +14,12 @@ import layerwise_weight_streaming_dit_amd as dlo
 
 def _bf16(a):
     return synth.bf16_bits_from_f32(np.asarray(a, np.float32))
+
+
+def _w(a):
+    """A parameter as the kernels read it from the slot: drawn as bf16 (as
+    streamed), converted to fp16 patterns the way the reconstruction does."""
+    return OS.as_f16_bits(_bf16(a))
 
 
 def _f16(a):
@@ -45,7 +51,7 @@ def test_assemble_bit_exact(n, dst_off, src_off):
     dlo.op_assemble(d[dst_off:], s[src_off:], n)
     t.cuda.synchronize()
     out = host(d, np.uint16)
-    assert np.array_equal(out[dst_off:dst_off + n], src[src_off:src_off + n])
+    assert_reconstructed(out[dst_off:dst_off + n], src[src_off:src_off + n])
     assert np.all(out[:dst_off] == 0xFFFF) and np.all(out[dst_off + n:] == 0xFFFF)
 
 
@@ -54,13 +60,13 @@ def test_assemble_bit_exact(n, dst_off, src_off):
 @pytest.mark.parametrize("d,c", [(256, 256), (2048, 256), (3072, 64)])
 def test_adaln(d, c):
     rng = np.random.default_rng(d + c)
-    w = _bf16(rng.standard_normal((6 * d, c)) * 0.02)
-    b = _bf16(rng.standard_normal(6 * d) * 0.02)
+    w = _w(rng.standard_normal((6 * d, c)) * 0.02)
+    b = _w(rng.standard_normal(6 * d) * 0.02)
     cond = rng.standard_normal(c).astype(np.float32)
     t = torch()
     mod = t.empty(6 * d, dtype=t.float32, device="cuda")
     dlo.op_adaln(dev(w), dev(b), dev(cond), mod, 6 * d, c)
-    want = bf16_to_f64(w).reshape(6 * d, c) @ D.silu(cond.astype(np.float64)) + bf16_to_f64(b)
+    want = f16_to_f64(w).reshape(6 * d, c) @ D.silu(cond.astype(np.float64)) + f16_to_f64(b)
     ok, ma, mr = within(host(mod), want, rtol=1e-4, atol=1e-5)
     assert ok, (ma, mr)
 
@@ -70,13 +76,13 @@ def test_adaln_ragged_rows(rows, c):
     # row counts that leave a workgroup's last rows empty (16 rows per
     # workgroup, 4 per wave) and widths from one lane group to the LDS limit
     rng = np.random.default_rng(rows * 7 + c)
-    w = _bf16(rng.standard_normal((rows, c)) * 0.02)
-    b = _bf16(rng.standard_normal(rows) * 0.02)
+    w = _w(rng.standard_normal((rows, c)) * 0.02)
+    b = _w(rng.standard_normal(rows) * 0.02)
     cond = rng.standard_normal(c).astype(np.float32)
     mod = dev(np.full(rows + 16, np.nan, np.float32))
     dlo.op_adaln(dev(w), dev(b), dev(cond), mod, rows, c)
     got = host(mod)
-    want = bf16_to_f64(w).reshape(rows, c) @ D.silu(cond.astype(np.float64)) + bf16_to_f64(b)
+    want = f16_to_f64(w).reshape(rows, c) @ D.silu(cond.astype(np.float64)) + f16_to_f64(b)
     ok, ma, mr = within(got[:rows], want, rtol=1e-4, atol=1e-5)
     assert ok, (ma, mr)
     assert np.all(np.isnan(got[rows:])), "wrote past the last row"
@@ -120,7 +126,8 @@ def _padded(rows_bits, ld):
 
 def _gemm_case(epi, M, N, K, w_rows=None, seed=0, pad=None):
     """One GEMM through the C ABI; `a` is the fp16 activation and `w` the
-    bf16 weight, except for the transposed-v epilogue where the roles swap.
+    weight (bf16 draws as the slot holds them, fp16), except for the
+    transposed-v epilogue where the roles swap.
     pad = (extra lda, extra ldw, extra ldo): the operands' row padding holds
     NaN (a read of it would poison the result) and the output's a sentinel
     that must survive."""
@@ -130,10 +137,10 @@ def _gemm_case(epi, M, N, K, w_rows=None, seed=0, pad=None):
     vt = epi == dlo.EPI_VT_F16
     a_val = rng.standard_normal((M, K)) * (0.02 if vt else 1.0)
     w_val = rng.standard_normal((w_rows, K)) * (1.0 if vt else 0.02)
-    a = _bf16(a_val) if vt else _f16(a_val)
-    w = _f16(w_val) if vt else _bf16(w_val)
+    a = _w(a_val) if vt else _f16(a_val)
+    w = _f16(w_val) if vt else _w(w_val)
     nb = M if vt else N
-    bias = _bf16(rng.standard_normal(nb) * 0.1)
+    bias = _w(rng.standard_normal(nb) * 0.1)
     gate = rng.standard_normal(N).astype(np.float32)
     x0 = rng.standard_normal((M, N)).astype(np.float32)
     if epi == dlo.EPI_GATED_F32:
@@ -148,10 +155,9 @@ def _gemm_case(epi, M, N, K, w_rows=None, seed=0, pad=None):
         got_all = host(out) if epi == dlo.EPI_GATED_F32 else host(out, np.uint16)
         assert np.array_equal(got_all[:, N:], out_h[:, N:]), "output padding was written"
         out = out[:, :N]
-    wf = f16_to_f64(w) if vt else bf16_to_f64(w)
-    wfull = wf[np.minimum(np.arange(N), w_rows - 1)]
-    acc = (bf16_to_f64(a) if vt else f16_to_f64(a)) @ wfull.T
-    bf = bf16_to_f64(bias)
+    wfull = f16_to_f64(w)[np.minimum(np.arange(N), w_rows - 1)]
+    acc = f16_to_f64(a) @ wfull.T
+    bf = f16_to_f64(bias)
     if epi == dlo.EPI_BIAS_F16:
         return f16_to_f64(host(out, np.uint16)), acc + bf
     if epi == dlo.EPI_BIAS_GELU_F16:
@@ -191,7 +197,7 @@ def test_gemm_strided_operands(epi, M, N, K):
 
 
 def test_gemm_epilogue_rounding_is_rne_exact():
-    """A one-hot A makes acc = w[j][i] exactly (the bf16 weights widen to
+    """A one-hot A makes acc = w[j][i] exactly (the bf16 weights convert to
     fp16 exactly); with bias of similar magnitude acc + bias is exact in
     fp32, so the fp16 output must be the round-to-nearest-even of that sum,
     bit for bit (ties included)."""
@@ -201,17 +207,17 @@ def test_gemm_epilogue_rounding_is_rne_exact():
     a[np.arange(M), np.arange(M) % K] = 1.0
     # w and bias: bf16 values whose fp32 sum has bits below bf16 precision,
     # including values exactly halfway between two fp16 numbers
-    w = _bf16((rng.integers(-256, 256, size=(N, K)) / 64.0).astype(np.float32))
+    w = _w((rng.integers(-256, 256, size=(N, K)) / 64.0).astype(np.float32))
     # bias: +-(1 + m/128) * 2^e, e in [-8, -5] -- exact bf16, so every fp32
     # sum w + bias spans at most 17 significant bits (exact)
     mant = 1.0 + rng.integers(0, 128, size=N) / 128.0
-    bias = _bf16((rng.choice([-1.0, 1.0], size=N) * mant * 2.0 ** rng.integers(-8, -4, size=N)).astype(np.float32))
+    bias = _w((rng.choice([-1.0, 1.0], size=N) * mant * 2.0 ** rng.integers(-8, -4, size=N)).astype(np.float32))
     t = torch()
     out = t.empty((M, N), dtype=t.int16, device="cuda")
     dlo.op_gemm(dlo.EPI_BIAS_F16, dev(_f16(a)), K, dev(w), K, N, dev(bias), None, out, N, M, N, K)
-    acc = bf16_to_f64(w)[:, np.arange(M) % K].T.astype(np.float32)
-    exact = acc + bf16_to_f64(bias).astype(np.float32)[None, :]
-    assert np.all(exact.astype(np.float64) == bf16_to_f64(w)[:, np.arange(M) % K].T + bf16_to_f64(bias)[None, :])
+    acc = f16_to_f64(w)[:, np.arange(M) % K].T.astype(np.float32)
+    exact = acc + f16_to_f64(bias).astype(np.float32)[None, :]
+    assert np.all(exact.astype(np.float64) == f16_to_f64(w)[:, np.arange(M) % K].T + f16_to_f64(bias)[None, :])
     want = exact.astype(np.float16).view(np.uint16)  # numpy rounds half to even
     ties = (exact.view(np.uint32) & 0x1FFF) == 0x1000  # halfway between two fp16 values
     assert np.any(ties)
@@ -248,9 +254,9 @@ def test_gemm_long_k_and_ragged_large_tiles(epi, M, N, K):
     rng = np.random.default_rng(M + N + K + epi)
     vt = epi == dlo.EPI_VT_F16
     w_rows = N - 77 if vt else N  # transposed v: columns past the last token repeat it
-    a = _bf16(rng.standard_normal((M, K)) * 0.02) if vt else _f16(rng.standard_normal((M, K)))
-    w = _f16(rng.standard_normal((w_rows, K))) if vt else _bf16(rng.standard_normal((N, K)) * 0.02)
-    bias = _bf16(rng.standard_normal(M if vt else N) * 0.1)
+    a = _w(rng.standard_normal((M, K)) * 0.02) if vt else _f16(rng.standard_normal((M, K)))
+    w = _f16(rng.standard_normal((w_rows, K))) if vt else _w(rng.standard_normal((N, K)) * 0.02)
+    bias = _w(rng.standard_normal(M if vt else N) * 0.1)
     gate = rng.standard_normal(N).astype(np.float32)
     x0 = rng.standard_normal((M, N)).astype(np.float32)
     t = torch()
@@ -259,11 +265,11 @@ def test_gemm_long_k_and_ragged_large_tiles(epi, M, N, K):
     rows = np.unique(np.concatenate([rng.choice(M, 48, replace=False), np.arange(M // 256 * 256, M)]))
     if vt:
         wf = f16_to_f64(w).reshape(w_rows, K)[np.minimum(np.arange(N), w_rows - 1)]
-        acc = bf16_to_f64(a[rows]).reshape(len(rows), K) @ wf.T + bf16_to_f64(bias)[rows][:, None]
+        acc = f16_to_f64(a[rows]).reshape(len(rows), K) @ wf.T + f16_to_f64(bias)[rows][:, None]
         got = f16_to_f64(host(out, np.uint16))[rows][:, vt_position(np.arange(N))]
         want = acc
     else:
-        acc = f16_to_f64(a[rows]) @ bf16_to_f64(w).reshape(N, K).T + bf16_to_f64(bias)
+        acc = f16_to_f64(a[rows]) @ f16_to_f64(w).reshape(N, K).T + f16_to_f64(bias)
         if epi == dlo.EPI_GATED_F32:
             got = host(out).astype(np.float64)[rows]
             want = x0[rows].astype(np.float64) + gate.astype(np.float64) * acc

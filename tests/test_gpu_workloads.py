@@ -8,7 +8,7 @@ import pytest
 
 import synth
 from oracle import dit as D, layout as OL, shard as OS
-from gpu_util import run_forward, sample_rows, within
+from gpu_util import assert_reconstructed, run_forward, sample_rows, within
 
 pytestmark = pytest.mark.gpu
 
@@ -22,7 +22,7 @@ def _block_check(wl, b, T, dp, rows=40, flags=0):
     cond = synth.conditioning(shp.d_cond)
     ctx = dlo.StreamedDiT([shp], dp, T, flags=flags)
     ctx.load_shards(0, flat)
-    assert np.array_equal(ctx.debug_assemble(0), flat)
+    assert_reconstructed(ctx.debug_assemble(0), flat)
     got = run_forward(ctx, x, cond)
     ctx.close()
     idx = sample_rows(T, rows, b + T)

@@ -114,3 +114,44 @@ def test_pages_memory_facts():
         assert dp * model_gb == pytest.approx(float(unsharded))
         assert dp * s * 2 / 1e9 == pytest.approx(float(sharded), rel=1e-9)
         assert s * 2 / 1e9 == pytest.approx(float(per_rank), rel=1e-9)
+
+
+def test_as_f16_bits_every_bf16_pattern_against_struct():
+    """All 65536 bf16 patterns: the oracle's conversion agrees with CPython's
+    own binary16 packing (struct format 'e', round half to even), which
+    raises for values too large for fp16; those must become infinities, and
+    NaNs must stay NaNs."""
+    import struct
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = O.as_f16_bits(bits)
+    vals = (bits.astype(np.uint32) << 16).view(np.float32)
+    for b, v, g in zip(bits.tolist(), vals.tolist(), got.tolist()):
+        if math.isnan(v):
+            assert (g & 0x7C00) == 0x7C00 and (g & 0x03FF) != 0, hex(b)
+            continue
+        try:
+            want = struct.unpack("<H", struct.pack("<e", v))[0]
+        except OverflowError:
+            want = 0xFC00 if v < 0 else 0x7C00
+        assert g == want, (hex(b), v, hex(g), hex(want))
+
+
+def test_as_f16_bits_special_cases():
+    """Hand-derived values: exact conversions, the subnormal grid (spacing
+    2^-24) with ties to even, and overflow."""
+    def bf16_of(x):
+        return np.array([np.float32(x).view(np.uint32) >> 16], np.uint16)
+    cases = [
+        (1.0, 0x3C00), (-2.0, 0xC000), (0.0, 0x0000), (-0.0, 0x8000),
+        (2.0 ** -14, 0x0400),          # smallest fp16 normal
+        (2.0 ** -17, 0x0080),          # subnormal, exact (8 significant bits fit)
+        (2.0 ** -24, 0x0001),          # smallest fp16 subnormal
+        (2.0 ** -25, 0x0000),          # a tie between 0 and 2^-24: to even (0)
+        (1.5 * 2.0 ** -25, 0x0001),    # above the tie: up
+        (3.0 * 2.0 ** -25, 0x0002),    # 1.5 * 2^-24, a tie: to even (2 * 2^-24)
+        (65280.0, 0x7BF8),             # the largest bf16 value below 65504: exact
+        (65536.0, 0x7C00),             # beyond fp16's range: infinity
+        (-65536.0, 0xFC00),
+    ]
+    for x, want in cases:
+        assert int(O.as_f16_bits(bf16_of(x))[0]) == want, (x, hex(int(O.as_f16_bits(bf16_of(x))[0])))

@@ -2,9 +2,9 @@
 operands and fp16 activations between kernels instead of bf16), on the CPU.
 
 The spec wording names bf16 GEMMs; the release page's B300 results run
-BF16.  The streamed weights here stay the pages' bf16 bits (widened exactly
-to fp16 in registers); what differs is the rounding of the activations
-between kernels.  Two facts decide it, both checked here:
+BF16.  The streamed weights here stay the pages' bf16 bits (the
+reconstruction converts them exactly to fp16 for the matrix cores); what
+differs is the rounding of the activations between kernels.  Two facts decide it, both checked here:
 
 * accuracy: emulating the kernels' rounding points on the widest block
   (d 8192, MLP 32768) shows bf16 activations exceed the 2e-2 output
