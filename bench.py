@@ -21,7 +21,9 @@ consecutive forwards and a serialized pass (dlo_set_flags between them).
 Prints ONE JSON line: blocks/s as ``value`` plus tokens/s, H2D GB/s, GEMM
 MFMA utilisation, overlap, per-step overheads, device weight residency, a
 roofline of the dominant kernel (timed with HIP events on the compute stream
-inside the timed region) and the oracle timed on the host cores.
+around that kernel only, inside the timed region; the warm-up, traced in
+full, names it, and per-kernel statistics come from a fully traced pass after
+the timed steps) and the oracle timed on the host cores.
 """
 from __future__ import annotations
 
@@ -336,14 +338,70 @@ def main():
             for t_req in Ts:
                 ctx.forward(xbuf, cond, t_req)
 
-    # ---- timed region: HIP events only on the compute stream (around each
-    # kernel), created before timing starts
-    ctx.reserve_trace((args.warmup + args.steps) * repeats * len(Ts))
+    def kernel_stats(tr, kinds):
+        """Per-kernel launch statistics of the traced forwards in tr."""
+        f_first = min((r["forward"] for r in tr), default=0)
+
+        def t_of(r):  # token count of a traced forward (the steps cycle through the requests)
+            return Ts[(r["forward"] - f_first) % len(Ts)]
+
+        def step_of(r):
+            return (r["forward"] - f_first) // (len(Ts) * max(repeats, 1))
+
+        by = {}
+        for r in tr:
+            if r["kind"] in kinds:
+                by.setdefault(r["kind"], []).append(r)
+        out = {}
+        for kind in kinds:
+            rs = by.get(kind, [])
+            if not rs:
+                continue
+            ds = sorted(r["end"] - r["start"] for r in rs)
+            avg = sum(ds) / len(ds)
+            med = ds[len(ds) // 2]
+            # work per launch follows each launch's block (widths differ
+            # between blocks in the irregular workload); average work /
+            # average time
+            unit = kernel_work(shapes[0], T)[kind][0]
+            work = sum(kernel_work(shapes[r["block"]], t_of(r))[kind][1] for r in rs) / len(rs)
+            e = {"launches": len(rs), "avg_ms": avg, "median_ms": med, "max_ms": ds[-1], "total_ms": sum(ds),
+                 "work_per_launch": work, "desc": KERNEL_DESC[kind],
+                 "launches_over_1_5x_median": sum(1 for x in ds if x > 1.5 * med),
+                 # the slowest launches: (step of the pass, block, ms)
+                 "slowest": [[step_of(r), r["block"], round(r["end"] - r["start"], 4)]
+                             for r in sorted(rs, key=lambda r: r["start"] - r["end"])[:4]]}
+            # average launch per step of the pass (a slow stretch shows as one step)
+            per_step = {}
+            for r in rs:
+                per_step.setdefault(step_of(r), []).append(r["end"] - r["start"])
+            e["avg_ms_by_step"] = [round(sum(v) / len(v), 4) for _, v in sorted(per_step.items())]
+            if unit == "flop":
+                e["TFLOPs"] = work / (avg * 1e-3) / 1e12
+                e["mfma_frac"] = e["TFLOPs"] / PEAK_BF16_TFLOPS
+            else:
+                e["GBps"] = work / (avg * 1e-3) / 1e9
+                e["hbm_frac"] = e["GBps"] / PEAK_HBM_GBPS
+            out[kind] = e
+        return out
+
+    # ---- warm-up, every kernel traced: it names the dominant kernel (the
+    # largest median launch time x launches; the first step's cold launches
+    # do not decide it)
+    ctx.reserve_trace(args.warmup * repeats * len(Ts))
     for i in range(args.warmup):
         step()
         torch.cuda.synchronize()
         log(f"warm-up step {i + 1}/{args.warmup} done")
-    ctx.trace()  # kernel intervals accumulate until read: drop the warm-up's
+    wk = kernel_stats(ctx.trace(), KERNEL_KINDS)
+    dom = max(wk, key=lambda k: wk[k]["median_ms"] * wk[k]["launches"]) if wk else "k_fc1"
+
+    # ---- timed region: HIP events on the compute stream around the dominant
+    # kernel only (each event pair between two kernels costs the stream a
+    # little; the per-kernel statistics come from a separate pass below),
+    # created before timing starts
+    ctx.set_trace_kinds(1 << dlo.IV_KIND[dom])
+    ctx.reserve_trace(args.steps * repeats * len(Ts))
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ts = time.perf_counter()
@@ -355,67 +413,36 @@ def main():
     elapsed = time.perf_counter() - ts
     ms_per_step = 1e3 * elapsed / args.steps
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (events {ev0.elapsed_time(ev1) / args.steps:.3f})")
-    ktr = ctx.trace()
+    timed_dom = kernel_stats(ctx.trace(), [dom])[dom]
 
-    # token count of each traced forward (the timed forwards cycle through
-    # the requests in order)
-    f_first = min((r["forward"] for r in ktr), default=0)
-
-    def t_of(r):
-        return Ts[(r["forward"] - f_first) % len(Ts)]
-
-    kernels = {}
-    by = {}
-    for r in ktr:
-        if r["kind"].startswith("k_"):
-            by.setdefault(r["kind"], []).append(r)
-    for kind in KERNEL_KINDS:
-        rs = by.get(kind, [])
-        if not rs:
-            continue
-        ds = sorted(r["end"] - r["start"] for r in rs)
-        avg = sum(ds) / len(ds)
-        med = ds[len(ds) // 2]
-        # work per launch follows each launch's block (widths differ between
-        # blocks in the irregular workload); average work / average time
-        unit = kernel_work(shapes[0], T)[kind][0]
-        work = sum(kernel_work(shapes[r["block"]], t_of(r))[kind][1] for r in rs) / len(rs)
-        e = {"launches": len(rs), "avg_ms": avg, "median_ms": med, "max_ms": ds[-1], "total_ms": sum(ds),
-             "work_per_launch": work, "desc": KERNEL_DESC[kind],
-             "launches_over_1_5x_median": sum(1 for x in ds if x > 1.5 * med),
-             # the slowest launches: (timed step, block, ms)
-             "slowest": [[(r["forward"] - f_first) // (len(Ts) * max(repeats, 1)), r["block"],
-                          round(r["end"] - r["start"], 4)]
-                         for r in sorted(rs, key=lambda r: r["start"] - r["end"])[:4]]}
-        # average launch per timed step (a slow stretch shows as one step)
-        per_step = {}
-        for r in rs:
-            per_step.setdefault((r["forward"] - f_first) // (len(Ts) * max(repeats, 1)), []).append(r["end"] - r["start"])
-        e["avg_ms_by_step"] = [round(sum(v) / len(v), 4) for _, v in sorted(per_step.items())]
-        if unit == "flop":
-            e["TFLOPs"] = work / (avg * 1e-3) / 1e12
-            e["mfma_frac"] = e["TFLOPs"] / PEAK_BF16_TFLOPS
-        else:
-            e["GBps"] = work / (avg * 1e-3) / 1e9
-            e["hbm_frac"] = e["GBps"] / PEAK_HBM_GBPS
-        kernels[kind] = e
+    # ---- every kernel traced, over up to two more steps: per-kernel statistics
+    n_k = max(1, min(2, args.steps))
+    ctx.set_trace_kinds(dlo.TRACE_KINDS_ALL)
+    ctx.reserve_trace(n_k * repeats * len(Ts))
+    torch.cuda.synchronize()
+    for _ in range(n_k):
+        step()
+    torch.cuda.synchronize()
+    kernels = kernel_stats(ctx.trace(), KERNEL_KINDS)
+    log(f"kernel statistics over {n_k} more steps, every kernel traced")
     gemm_kinds = [k for k in ("k_qk", "k_v", "k_out", "k_fc1", "k_fc2") if k in kernels]
     gemm_flops = sum(kernels[k]["work_per_launch"] * kernels[k]["launches"] for k in gemm_kinds)
     gemm_ms = sum(kernels[k]["total_ms"] for k in gemm_kinds)
     gemm_util = gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS if gemm_ms else None
-    dom = max(kernels, key=lambda k: kernels[k]["total_ms"])
-    unit, work = kernel_work(shapes[0], T)[dom][0], kernels[dom]["work_per_launch"]
+    unit, work = kernel_work(shapes[0], T)[dom][0], timed_dom["work_per_launch"]
     peak = PEAK_BF16_TFLOPS if unit == "flop" else PEAK_HBM_GBPS
     scale = 1e12 if unit == "flop" else 1e9
-    ach = work / (kernels[dom]["avg_ms"] * 1e-3) / scale
-    ach_med = work / (kernels[dom]["median_ms"] * 1e-3) / scale
+    ach = work / (timed_dom["avg_ms"] * 1e-3) / scale
+    ach_med = work / (timed_dom["median_ms"] * 1e-3) / scale
     roofline = {"bound": "mfma" if unit == "flop" else "hbm", "achieved": ach, "peak": peak,
                 "unit": "TFLOP/s" if unit == "flop" else "GB/s", "frac": ach / peak,
                 "traffic": traffic_from_profiles(dom, wl.name),
-                "kernel": f"{dom}: {KERNEL_DESC[dom]}", "avg_launch_ms": kernels[dom]["avg_ms"],
-                "median_launch_ms": kernels[dom]["median_ms"], "max_launch_ms": kernels[dom]["max_ms"],
-                "frac_by_median": ach_med / peak, "launches": kernels[dom]["launches"],
-                "work_per_launch": work, "work_unit": unit}
+                "kernel": f"{dom}: {KERNEL_DESC[dom]}", "avg_launch_ms": timed_dom["avg_ms"],
+                "median_launch_ms": timed_dom["median_ms"], "max_launch_ms": timed_dom["max_ms"],
+                "frac_by_median": ach_med / peak, "launches": timed_dom["launches"],
+                "launches_over_1_5x_median": timed_dom["launches_over_1_5x_median"],
+                "work_per_launch": work, "work_unit": unit,
+                "timing": "HIP events around this kernel only, every launch of the timed steps"}
 
     # ---- untraced pass: host dispatch per step and the untraced step time
     ctx.set_flags(0)
@@ -558,6 +585,8 @@ def main():
         "overlap": dict(sched or {}, serialized_ms_per_step=serial),
         "residency": residency,
         "kernels": kernels,
+        "kernels_pass": f"{n_k} step(s) after the timed region with every kernel traced (the timed steps "
+                        f"carry events around the dominant kernel only)",
         "roofline": roofline,
         "cpu_baseline": cpu,
         "setup_s": load_s,

@@ -322,6 +322,18 @@ DLO_API dlo_status dlo_destroy(dlo_ctx* ctx);
  * unknown flag, DLO_E_POISONED. */
 DLO_API dlo_status dlo_set_flags(dlo_ctx* ctx, uint32_t flags);
 
+/* Restrict the intervals that tracing records to the kinds whose bit is set
+ * in `kinds` (bit n records DLO_IV kind n; DLO_TRACE_KINDS_ALL, the default,
+ * records every kind).  A timed run can then carry HIP events around only
+ * the kernel it measures: every event pair recorded between two kernels
+ * costs the compute stream a little time.  Applies to the forwards enqueued
+ * after this call, under DLO_FLAG_TRACE or DLO_FLAG_TRACE_KERNELS; the
+ * summary figures of dlo_get_stats need the H2D, reconstruction and compute
+ * kinds.  Drops recorded intervals.  Errors: DLO_E_INVAL for a bit past
+ * DLO_IV_K_FC2, DLO_E_POISONED. */
+#define DLO_TRACE_KINDS_ALL 0xFFFu
+DLO_API dlo_status dlo_set_trace_kinds(dlo_ctx* ctx, uint32_t kinds);
+
 /* Create, ahead of time, the timing events that `forwards` traced forwards
  * under the current flags need, so that no event is created while they are
  * enqueued (creating events mid-run perturbs the timings).  Errors:

@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     ABI_VERSION, DloError, StreamedDiT, block_layout, required_bytes, lib, check,
     op_assemble, op_adaln, op_ln_modulate, op_gemm, op_attention,
     FLAG_TRACE, FLAG_SERIALIZE, FLAG_POISON_SLOTS, FLAG_TRACE_KERNELS, FLAG_TRACE_SPAN,
+    IV_KIND, TRACE_KINDS_ALL,
     EPI_BIAS_F16, EPI_BIAS_GELU_F16, EPI_GATED_F32, EPI_VT_F16,
     OK, E_INVAL, E_SHAPE, E_STATE, E_HOST_OOM, E_DEV_OOM, E_HIP, E_POISONED,
 )

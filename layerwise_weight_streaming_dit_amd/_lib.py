@@ -25,6 +25,8 @@ FLAG_TRACE, FLAG_SERIALIZE, FLAG_POISON_SLOTS, FLAG_TRACE_KERNELS, FLAG_TRACE_SP
 IV_H2D, IV_ASM, IV_COMPUTE = 0, 1, 2
 IV_NAMES = {0: "h2d", 1: "asm", 2: "compute", 3: "k_adaln", 4: "k_ln1", 5: "k_qk", 6: "k_v", 7: "k_attn",
             8: "k_out", 9: "k_ln2", 10: "k_fc1", 11: "k_fc2"}
+IV_KIND = {name: kind for kind, name in IV_NAMES.items()}
+TRACE_KINDS_ALL = 0xFFF
 EPI_BIAS_F16, EPI_BIAS_GELU_F16, EPI_GATED_F32, EPI_VT_F16 = 0, 1, 2, 3
 
 
@@ -87,6 +89,7 @@ _SIGNATURES = {
     "dlo_destroy": [_P],
     "dlo_set_flags": [_P, ctypes.c_uint32],
     "dlo_reserve_trace": [_P, _I32],
+    "dlo_set_trace_kinds": [_P, ctypes.c_uint32],
     "dlo_layout": [_P, _I32, ctypes.POINTER(_I64), ctypes.POINTER(_I64), ctypes.POINTER(_I32),
                    ctypes.POINTER(ParamDesc), _I32],
     "dlo_get_shard": [_P, _I32, _I32, ctypes.POINTER(_P), ctypes.POINTER(_I64)],
@@ -258,6 +261,12 @@ class StreamedDiT:
         recorded intervals)."""
         check(lib().dlo_set_flags(self._h, flags))
         self.flags = flags
+
+    def set_trace_kinds(self, kinds: int) -> None:
+        """Record only the interval kinds whose bit is set (bit n = kind n of
+        IV_NAMES; TRACE_KINDS_ALL records all) in the traced forwards enqueued
+        from now on (drops any recorded intervals)."""
+        check(lib().dlo_set_trace_kinds(self._h, kinds))
 
     def reserve_trace(self, forwards: int) -> None:
         """Create the timing events `forwards` traced forwards need now, so

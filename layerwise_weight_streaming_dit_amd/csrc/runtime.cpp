@@ -164,6 +164,7 @@ size_t carve_workspace(char* base, size_t T, size_t d, size_t m, bool mixed, Wor
 struct dlo_ctx {
   int device = 0;
   uint32_t flags = 0;
+  uint32_t trace_kinds = DLO_TRACE_KINDS_ALL;  // interval kinds recorded when tracing
   int dp = 1;
   int max_tokens = 1;
   int d_max = 0, m_max = 0;
@@ -319,12 +320,19 @@ void copy_parallel(void* dst, const void* src, size_t bytes) {
 int fwd_index(const dlo_ctx* ctx) { return static_cast<int>(ctx->forwards); }
 
 // Trace events one forward records under the context's current flags.
+// Whether intervals of `kind` (DLO_IV_*) are recorded.
+bool traced(const dlo_ctx* ctx, int kind) { return (ctx->trace_kinds >> kind) & 1u; }
+
 size_t events_per_forward(const dlo_ctx* ctx) {
   const bool all = (ctx->flags & DLO_FLAG_TRACE) != 0;
   const bool kern = all || (ctx->flags & DLO_FLAG_TRACE_KERNELS) != 0;
   if (!kern) return 0;
+  int kinds = 0;
+  for (int kind = DLO_IV_K_ADALN; kind <= DLO_IV_K_FC2; ++kind) kinds += traced(ctx, kind) ? 1 : 0;
+  const size_t per_chunk = all ? 2 * ((traced(ctx, DLO_IV_H2D) ? 1 : 0) + (traced(ctx, DLO_IV_ASM) ? 1 : 0)) : 0;
   size_t n = 0;
-  for (auto& b : ctx->blocks) n += 2 + 2 * 9 + (all ? 4 * b.chunks.size() : 0);
+  for (auto& b : ctx->blocks)
+    n += (traced(ctx, DLO_IV_COMPUTE) ? 2 : 0) + 2 * kinds + per_chunk * b.chunks.size();
   return n;
 }
 
@@ -388,12 +396,12 @@ dlo_status enqueue_staging(dlo_ctx* ctx, int b, int k, bool trace, bool in_forwa
       DLO_HIP(ctx, hipStreamWaitEvent(cs, ctx->comp_done[k ^ 1], 0));
     }
     TraceEv tv{};
-    if (trace) {
+    if (trace && traced(ctx, DLO_IV_H2D)) {
       tv = TraceEv{DLO_IV_H2D, b, static_cast<int>(ci), -1, lb, fwd_index(ctx), c.len * 2, next_ev(ctx), next_ev(ctx)};
       if (tv.start) DLO_HIP(ctx, hipEventRecord(tv.start, cs));
     }
     DLO_HIP(ctx, hipMemcpyAsync(land, blk.pinned + c.off, size_t(c.len) * 2, hipMemcpyHostToDevice, cs));
-    if (trace && tv.end) {
+    if (tv.end) {
       DLO_HIP(ctx, hipEventRecord(tv.end, cs));
       ctx->trace.push_back(tv);
     }
@@ -406,12 +414,12 @@ dlo_status enqueue_staging(dlo_ctx* ctx, int b, int k, bool trace, bool in_forwa
     }
     DLO_HIP(ctx, hipStreamWaitEvent(ctx->gather_s, ctx->h2d_done[lb], 0));
     TraceEv ta{};
-    if (trace) {
+    if (trace && traced(ctx, DLO_IV_ASM)) {
       ta = TraceEv{DLO_IV_ASM, b, static_cast<int>(ci), k, lb, fwd_index(ctx), c.valid * 2, next_ev(ctx), next_ev(ctx)};
       if (ta.start) DLO_HIP(ctx, hipEventRecord(ta.start, ctx->gather_s));
     }
     DLO_HIP(ctx, launch_assemble(ctx->slot[k] + c.off, land, c.valid, ctx->gather_s));
-    if (trace && ta.end) {
+    if (ta.end) {
       DLO_HIP(ctx, hipEventRecord(ta.end, ctx->gather_s));
       ctx->trace.push_back(ta);
     }
@@ -446,12 +454,12 @@ dlo_status enqueue_block_compute(dlo_ctx* ctx, int b, int k, float*& x_cur, int&
   // Record a timed interval around one kernel when tracing.
   auto timed = [&](int kind, auto&& launch) -> dlo_status {
     TraceEv tv{};
-    if (trace) {
+    if (trace && traced(ctx, kind)) {
       tv = TraceEv{kind, b, -1, k, -1, fwd_index(ctx), 0, next_ev(ctx), next_ev(ctx)};
       if (tv.start) DLO_HIP(ctx, hipEventRecord(tv.start, s));
     }
     DLO_HIP(ctx, launch());
-    if (trace && tv.end) {
+    if (tv.end) {
       DLO_HIP(ctx, hipEventRecord(tv.end, s));
       ctx->trace.push_back(tv);
     }
@@ -713,13 +721,13 @@ dlo_status forward_impl(dlo_ctx* ctx, float* x, const float* cond, int32_t token
     if (st != DLO_OK) return st;
     DLO_HIP(ctx, hipStreamWaitEvent(stream, ctx->asm_done[k], 0));
     TraceEv tc{};
-    if (trace) {
+    if (trace && traced(ctx, DLO_IV_COMPUTE)) {
       tc = TraceEv{DLO_IV_COMPUTE, b, -1, k, -1, fwd_index(ctx), 0, next_ev(ctx), next_ev(ctx)};
       if (tc.start) DLO_HIP(ctx, hipEventRecord(tc.start, stream));
     }
     st = enqueue_block_compute(ctx, b, k, x_cur, d_cur, x, cond, tokens, stream, trace, w);
     if (st != DLO_OK) return st;
-    if (trace && tc.end) {
+    if (tc.end) {
       DLO_HIP(ctx, hipEventRecord(tc.end, stream));
       ctx->trace.push_back(tc);
     }
@@ -1040,6 +1048,16 @@ extern "C" DLO_API dlo_status dlo_set_flags(dlo_ctx* ctx, uint32_t flags) {
                               DLO_FLAG_TRACE_KERNELS | DLO_FLAG_TRACE_SPAN;
   if (flags & ~kKnown) return fail(DLO_E_INVAL, "unknown flags 0x%x", flags & ~kKnown);
   ctx->flags = flags;
+  drop_trace(ctx);
+  return DLO_OK;
+}
+
+extern "C" DLO_API dlo_status dlo_set_trace_kinds(dlo_ctx* ctx, uint32_t kinds) {
+  clear_error();
+  dlo_status st = check_ctx(ctx);
+  if (st != DLO_OK) return st;
+  if (kinds & ~DLO_TRACE_KINDS_ALL) return fail(DLO_E_INVAL, "unknown interval kinds 0x%x", kinds & ~DLO_TRACE_KINDS_ALL);
+  ctx->trace_kinds = kinds;
   drop_trace(ctx);
   return DLO_OK;
 }

@@ -399,6 +399,37 @@ void run_schedule_case(const std::vector<dlo_block_desc>& descs, int dp, int64_t
   destroy(c);
 }
 
+// dlo_set_trace_kinds: unknown kind bits are refused; a mask keeps only its
+// kinds in the kernel trace (one K_FC1 interval per block), and the full mask
+// brings every compute-stream interval back.
+void run_trace_kinds_case() {
+  Ctx c;
+  std::vector<dlo_block_desc> descs(3, dlo_block_desc{128, 2, 256, 64, 0, 0, nullptr});
+  CHECK(make(c, descs, 2, 8, 0, DLO_FLAG_TRACE_KERNELS) == DLO_OK);
+  if (!c.ctx) return;
+  CHECK(dlo_set_trace_kinds(c.ctx, 1u << 12) == DLO_E_INVAL);
+  CHECK(dlo_set_trace_kinds(nullptr, DLO_TRACE_KINDS_ALL) == DLO_E_INVAL);
+  auto kinds_of_forward = [&](std::vector<int>* per_kind) {
+    CHECK(dlo_forward(c.ctx, c.x.data(), c.cond.data(), 8, nullptr) == DLO_OK);
+    int32_t n = 0;
+    CHECK(dlo_get_trace(c.ctx, nullptr, 0, &n) == DLO_OK);
+    std::vector<dlo_interval> iv(n);
+    CHECK(dlo_get_trace(c.ctx, iv.data(), n, &n) == DLO_OK);
+    per_kind->assign(12, 0);
+    for (auto& v : iv)
+      if (v.kind >= 0 && v.kind < 12) ++(*per_kind)[v.kind];
+  };
+  std::vector<int> k;
+  CHECK(dlo_set_trace_kinds(c.ctx, 1u << DLO_IV_K_FC1) == DLO_OK);
+  kinds_of_forward(&k);
+  for (int kind = 0; kind < 12; ++kind) CHECK(k[kind] == (kind == DLO_IV_K_FC1 ? 3 : 0));
+  CHECK(dlo_set_trace_kinds(c.ctx, DLO_TRACE_KINDS_ALL) == DLO_OK);
+  kinds_of_forward(&k);
+  CHECK(k[DLO_IV_H2D] == 0 && k[DLO_IV_ASM] == 0 && k[DLO_IV_COMPUTE] == 3);
+  for (int kind = DLO_IV_K_ADALN; kind <= DLO_IV_K_FC2; ++kind) CHECK(k[kind] == 3);
+  destroy(c);
+}
+
 // A HIP error during a forward poisons the context: every later call fails
 // with DLO_E_POISONED, and destroy still succeeds.
 void run_fail_closed_case() {
@@ -432,6 +463,7 @@ int main() {
   run_schedule_case({small, wide, small}, 1024, 0, DLO_FLAG_TRACE);
   // one block, dp 1 (rank-local)
   run_schedule_case({wide}, 1, 4096, DLO_FLAG_POISON_SLOTS);
+  run_trace_kinds_case();
   run_fail_closed_case();
   if (g_failures) {
     fprintf(stderr, "%d check(s) failed\n", g_failures);

@@ -547,3 +547,30 @@ def test_kernel_trace_accumulates_until_read():
         assert sum(r["kind"] == "k_fc2" for r in tr) == n * wl.num_blocks
         assert all(r["end"] >= r["start"] >= 0.0 for r in tr)
     assert ctx.trace() == []
+
+
+def test_trace_kinds_keep_only_the_selected_kernel():
+    """dlo_set_trace_kinds: with only the MLP-up kind selected, a traced
+    forward records exactly one interval per block, of that kind, and its
+    output equals the fully traced forward's; unknown kind bits are refused."""
+    wl = synth.workload("tiny")
+    W = _weights(wl)
+    ctx = _ctx(list(wl.blocks), 4, wl.tokens, flags=dlo.FLAG_TRACE_KERNELS)
+    for b, flat in W.items():
+        ctx.load_shards(b, flat)
+    x, cond = synth.activations(wl.tokens, 256), synth.conditioning(256)
+    full = _run(ctx, x, cond)
+    assert len(ctx.trace()) == wl.num_blocks * 10
+    with pytest.raises(dlo.DloError) as e:
+        ctx.set_trace_kinds(1 << 12)
+    assert e.value.code == dlo.E_INVAL
+    ctx.set_trace_kinds(1 << dlo.IV_KIND["k_fc1"])
+    ctx.reserve_trace(2)
+    one = _run(ctx, x, cond)
+    tr = ctx.trace()
+    assert [r["kind"] for r in tr] == ["k_fc1"] * wl.num_blocks
+    assert sorted(r["block"] for r in tr) == list(range(wl.num_blocks))
+    assert np.array_equal(one, full)
+    ctx.set_trace_kinds(dlo.TRACE_KINDS_ALL)
+    _run(ctx, x, cond)
+    assert len(ctx.trace()) == wl.num_blocks * 10
