@@ -16,11 +16,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-// bf16 bit pattern -> fp32 (exact: bf16 is the upper half of an fp32).
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
-  return __uint_as_float(static_cast<uint32_t>(b) << 16);
-}
-
 // Two fp32 -> packed pair of fp16 (lo in bits 0..15), round to nearest even
 // (v_cvt_pk_f16_f32).  Activations between kernels are fp16.
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {

@@ -136,6 +136,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
       const char* src = reinterpret_cast<const char*>(pf_is_a[j] ? g.a : g.w) + pf_off[j] + koff;
 #if defined(__HIP_DEVICE_COMPILE__)
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)sPf, 4, 0, 0);
+#else
+      (void)src;  // the host pass only type-checks the kernel
+      (void)sPf;
 #endif
       __builtin_amdgcn_sched_barrier(0);
     }
