@@ -51,15 +51,7 @@ constexpr int kGroupM = 4;
 // (32 banks) or 16 (64 banks) consecutive rows on distinct banks.
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// PFD > 0: L2 prefetch at distance PFD -- during step kt one 4-byte load
-// touches every 128-byte line of step kt + PFD, so the step's own loads
-// (issued one step ahead, straight into LDS) hit in L2 when the operands come
-// from HBM instead of the last-level cache.  Used for the 256x128 tile, whose
-// long-K products (MLP down) otherwise stall on HBM latency: measured with
-// the caches flushed before each call, 4096x2048x8192 takes 208 us without it
-// and 167 us with it (150 vs 156 us with warm caches); the other tiles gained
-// nothing from it.
-template <int BM, int BN, int WM, int WN, int PFD, int EPI>
+template <int BM, int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
   constexpr int W = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -113,36 +105,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
   const __amdgpu_buffer_rsrc_t rs_a = buffer_rsrc(g.a, (static_cast<uint32_t>(g.M - 1) * g.lda + g.K) * 2u);
   const __amdgpu_buffer_rsrc_t rs_w = buffer_rsrc(g.w, (static_cast<uint32_t>(g.w_rows - 1) * g.ldw + g.K) * 2u);
 
-  // L2 prefetch: one 4-byte DMA per 128-byte line (row) of a step's A and W
-  // tiles, NPF per wave, landing in a scratch LDS word per lane that nothing
-  // reads.  Lanes past the last row repeat it.
-  constexpr int NPF = PFD > 0 ? (BM + BN + W * 64 - 1) / (W * 64) : 0;
-  __shared__ __attribute__((aligned(256))) uint32_t sPf[64];
-  uint32_t pf_off[NPF > 0 ? NPF : 1];
-  bool pf_is_a[NPF > 0 ? NPF : 1];
-#pragma unroll
-  for (int j = 0; j < NPF; ++j) {
-    const int li = min((j * W + wave) * 64 + lane, BM + BN - 1);
-    pf_is_a[j] = li < BM;
-    pf_off[j] = pf_is_a[j] ? static_cast<uint32_t>(min(m0 + li, g.M - 1)) * g.lda * 2u
-                           : static_cast<uint32_t>(min(n0 + li - BM, g.w_rows - 1)) * g.ldw * 2u;
-  }
-  auto prefetch = [&](int kstep) {
-    const uint32_t koff = static_cast<uint32_t>(min(kstep, nk - 1)) * (kBK * 2);
-#pragma unroll
-    for (int j = 0; j < NPF; ++j) {
-      // a global (FLAT) load here measured 2% faster than a buffer load on
-      // the MLP-down shape (4096x2048x8192)
-      const char* src = reinterpret_cast<const char*>(pf_is_a[j] ? g.a : g.w) + pf_off[j] + koff;
-#if defined(__HIP_DEVICE_COMPILE__)
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)sPf, 4, 0, 0);
-#else
-      (void)src;  // the host pass only type-checks the kernel
-      (void)sPf;
-#endif
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
 
   auto stageA = [&](auto S) -> uint16_t* {
     if constexpr (decltype(S)::value == 0) return sA0;
@@ -228,9 +190,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
         }
       }
     };
-    // loads return in issue order: all but the NPF prefetches issued after
-    // this step's loads (previous step) have landed
-    wait_vmcnt<NPF>();
+    // this step's loads (issued during the previous step) have landed
+    wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     read_frags(S, 0, fa0, fb0);
     wait_lgkmcnt0();
@@ -243,7 +204,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
     __builtin_amdgcn_sched_barrier(0);
     mfmas(fa1, fb1, [&](int tm) { dma_after(TM + tm); });
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (PFD > 0) prefetch(kt + PFD);
     wait_lgkmcnt0();
     read_frags(S, 3, fa1, fb1);
     __builtin_amdgcn_sched_barrier(0);
@@ -254,7 +214,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
   };
 
   issue(IC<0>{}, 0);
-  if constexpr (PFD > 0) prefetch(PFD - 1);  // keeps the per-step count of loads behind the stage's own
   // K is a multiple of two steps (128), so the ring unrolls without early exits
   for (int kt = 0; kt < nk; kt += 2) {
     step(IC<0>{}, kt);
@@ -400,15 +359,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// 256x256 tile with ONE wave per SIMD (four waves).  The waves split the
-// tile along the dimension of the activation operand, so each wave owns its
-// own slice of the weight operand (no two waves read the same weight
-// fragments):
-//   WM=1, WN=4: waves own 64 weight rows (columns of C), 256x64 per wave;
-//   WM=4, WN=1: the transposed v projection (weights are the A operand),
-//               waves own 64 weight rows, 64x256 per wave.
-// Per 64-wide K step a wave issues 64 MFMAs (256 fp32 accumulators per lane
-// in the accumulation registers) against 40 fragment reads.  With no second
+// 256 x BN tile with ONE wave per SIMD (four waves).
+//   BN = 256: the waves split the tile along the dimension of the activation
+//   operand, so each wave owns its own slice of the weight operand (no two
+//   waves read the same weight fragments):
+//     WM=1, WN=4: waves own 64 weight rows (columns of C), 256x64 per wave;
+//     WM=4, WN=1: the transposed v projection (weights are the A operand),
+//                 waves own 64 weight rows, 64x256 per wave.
+//   BN = 128 (the long-K shapes with too few 256x256 tiles): a 2 x 2 wave
+//   grid, 128x64 per wave.
+// Per 64-wide K step a BN = 256 wave issues 64 MFMAs (256 fp32 accumulators
+// per lane in the accumulation registers) against 40 fragment reads, a
+// BN = 128 wave 32 MFMAs against 24.  With no second
 // wave on the SIMD the stream is pipelined by hand:
 //   * the fragments of k slice j+1 are read one after each of slice j's
 //     first ten MFMAs; the stage loads are buffer loads (dma16_buf), so the
@@ -424,23 +386,24 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmArgs g) {
 //   * load addresses are a uniform base (scalar registers, advanced per step)
 //     plus a fixed per-lane offset; the LDS destination of every load is
 //     uniform too, so issuing a load costs no vector instruction.
-template <int WM, int WN, int EPI>
+template <int BN, int WM, int WN, int EPI>
 __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
-  constexpr int BM = 256, BN = 256, W = 4;
+  constexpr int BM = 256, W = 4;
   static_assert(WM * WN == W, "four waves");
   constexpr int WTM = BM / WM, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
-  constexpr int STAGE = BM * kBK;   // elements per operand per stage (32 KB)
-  constexpr int LA = BM / 8 / W;    // 1 KB DMA loads per wave per operand per stage (8)
-  constexpr int ND = 2 * LA;        // DMA loads per wave per step (16)
+  constexpr int MF = TM * TN;        // MFMAs per k slice
+  constexpr int STAGE_A = BM * kBK, STAGE_B = BN * kBK;
+  constexpr int LA = BM / 8 / W, LB = BN / 8 / W;  // 1 KB DMA loads per wave per operand per stage
+  constexpr int ND = LA + LB;        // DMA loads per wave per step
   constexpr bool A_IS_WEIGHT = EPI == EPI_VT_F16;
   constexpr int NWF = A_IS_WEIGHT ? TM : TN;  // weight fragments per slice
-  static_assert(NWF == 2, "each wave owns 64 weight rows");
+  static_assert(MF % NWF == 0 && TM + TN <= MF, "slice shape");
   static_assert(WTM % 64 == 0 && WTN % 64 == 0, "fragment addressing assumes an even tile count per wave");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t sA0[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint16_t sA1[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB0[STAGE];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[STAGE_A];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA1[STAGE_A];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[STAGE_B];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB1[STAGE_B];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
@@ -469,12 +432,17 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
   // ---- DMA sources: per-lane byte offsets (rows clamped in bounds) from a
   // uniform base; LDS slot s of a stage holds row s / 8, 16-byte chunk
   // (s % 8) ^ swz(row)
-  uint32_t ga[LA], gb[LA];
+  uint32_t ga[LA], gb[LB];
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
     const int slot = (wave * LA + i) * 64 + lane, row = slot >> 3;
     const int c = (slot & 7) ^ swz(row);
     ga[i] = (static_cast<uint32_t>(min(m0 + row, g.M - 1)) * g.lda + c * 8) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < LB; ++i) {
+    const int slot = (wave * LB + i) * 64 + lane, row = slot >> 3;
+    const int c = (slot & 7) ^ swz(row);
     gb[i] = (static_cast<uint32_t>(min(n0 + row, g.w_rows - 1)) * g.ldw + c * 8) * 2u;
   }
   const int nk = g.K / kBK;
@@ -498,7 +466,7 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
     if (d < LA)
       dma16_buf(rs_a, ga[d], kb, stageA(S) + (wave * LA + d) * 512);
     else
-      dma16_buf(rs_w, gb[d - LA], kb, stageB(S) + (wave * LA + d - LA) * 512);
+      dma16_buf(rs_w, gb[d - LA], kb, stageB(S) + (wave * LB + d - LA) * 512);
   };
 
   f32x16_t acc[TM][TN];
@@ -569,9 +537,9 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
   auto mfma_slice = [&](auto P, auto&& dma, auto&& rd) {
     constexpr int p = decltype(P)::value;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < MF; ++i) {
       // weight fragment outer: each weight fragment is done with early
-      const int wf = i / (16 / NWF), af = i % (16 / NWF);
+      const int wf = i / (MF / NWF), af = i % (MF / NWF);
       const int tm = A_IS_WEIGHT ? wf : af, tn = A_IS_WEIGHT ? af : wf;
       acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(rb[p][tn], ra[p][tm], acc[tm][tn], 0, 0, 0);
       rd(i);
@@ -580,7 +548,10 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
     }
   };
 
-  constexpr int NEARLY = 10;
+  // DMA loads of the step after next issued in the slice after the barrier;
+  // the rest go out during the next step's first slice
+  constexpr int NEARLY = ND * 5 / 8;
+  static_assert(NEARLY <= MF && ND - NEARLY <= MF, "loads per slice");
   auto step = [&](auto S, int kt) {
     constexpr int s = decltype(S)::value;
     auto dma_range = [&](auto T, int kstep, int first, int count) {
@@ -725,42 +696,43 @@ __global__ __launch_bounds__(256) void gemm_wt_kernel(GemmArgs g) {
   }
 }
 
+template <int BN, int WM, int WN, int WMV, int WNV>
 hipError_t launch_wt(int epi, const GemmArgs& g, hipStream_t s) {
-  const int tiles = ((g.M + 255) / 256) * ((g.N + 255) / 256);
+  const int tiles = ((g.M + 255) / 256) * ((g.N + BN - 1) / BN);
   const dim3 grid(tiles), block(256);
   switch (epi) {
     case EPI_BIAS_F16:
-      hipLaunchKernelGGL((gemm_wt_kernel<1, 4, EPI_BIAS_F16>), grid, block, 0, s, g);
+      hipLaunchKernelGGL((gemm_wt_kernel<BN, WM, WN, EPI_BIAS_F16>), grid, block, 0, s, g);
       break;
     case EPI_BIAS_GELU_F16:
-      hipLaunchKernelGGL((gemm_wt_kernel<1, 4, EPI_BIAS_GELU_F16>), grid, block, 0, s, g);
+      hipLaunchKernelGGL((gemm_wt_kernel<BN, WM, WN, EPI_BIAS_GELU_F16>), grid, block, 0, s, g);
       break;
     case EPI_GATED_F32:
-      hipLaunchKernelGGL((gemm_wt_kernel<1, 4, EPI_GATED_F32>), grid, block, 0, s, g);
+      hipLaunchKernelGGL((gemm_wt_kernel<BN, WM, WN, EPI_GATED_F32>), grid, block, 0, s, g);
       break;
     default:
-      hipLaunchKernelGGL((gemm_wt_kernel<4, 1, EPI_VT_F16>), grid, block, 0, s, g);
+      hipLaunchKernelGGL((gemm_wt_kernel<BN, WMV, WNV, EPI_VT_F16>), grid, block, 0, s, g);
       break;
   }
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int PFD>
+template <int BM, int BN, int WM, int WN>
 hipError_t launch_shape(int epi, const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   const dim3 grid(tiles), block(WM * WN * 64);
   switch (epi) {
     case EPI_BIAS_F16:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, PFD, EPI_BIAS_F16>), grid, block, 0, s, g);
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI_BIAS_F16>), grid, block, 0, s, g);
       break;
     case EPI_BIAS_GELU_F16:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, PFD, EPI_BIAS_GELU_F16>), grid, block, 0, s, g);
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI_BIAS_GELU_F16>), grid, block, 0, s, g);
       break;
     case EPI_GATED_F32:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, PFD, EPI_GATED_F32>), grid, block, 0, s, g);
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI_GATED_F32>), grid, block, 0, s, g);
       break;
     default:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, PFD, EPI_VT_F16>), grid, block, 0, s, g);
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, EPI_VT_F16>), grid, block, 0, s, g);
       break;
   }
   return hipGetLastError();
@@ -773,14 +745,16 @@ hipError_t launch_gemm(int epilogue, const GemmArgs& g, hipStream_t s) {
   // From one 256x256 tile per CU up, the one-wave-per-SIMD kernel is ahead
   // (measured on warm operands, same results bit for bit: 1-9% on the image
   // shapes with one or two tiles per CU, 5-10% on the large and mid-video
-  // shapes).  The 256x128 tile (4 waves, one per SIMD) pays off only over a
-  // long K; for short K two 128x128 tiles per CU (8 waves) finish first
-  // (measured: 9% faster at 2048x4096x2048, 4% slower at 4096x2048x8192).
+  // shapes).  Its 256x128 form (2 x 2 waves) pays off over a long K (MLP
+  // down of the image block, 4096x2048x8192: 137 -> 127 us warm, 152 -> 144
+  // us by the median inside the forward, against the eight-wave-style
+  // 256x128 kernel with an L2 prefetch it replaces); for short K two 128x128
+  // tiles per CU (8 waves) finish first (2048x4096x2048: 34.5 vs 35.6 us).
   const int64_t t256 = static_cast<int64_t>((g.M + 255) / 256) * ((g.N + 255) / 256);
   const int64_t t256x128 = static_cast<int64_t>((g.M + 255) / 256) * ((g.N + 127) / 128);
-  if (t256 >= 256) return launch_wt(epilogue, g, s);
-  if (t256x128 >= 256 && g.K >= 4096) return launch_shape<256, 128, 2, 2, 2>(epilogue, g, s);
-  return launch_shape<128, 128, 2, 2, 0>(epilogue, g, s);
+  if (t256 >= 256) return launch_wt<256, 1, 4, 4, 1>(epilogue, g, s);
+  if (t256x128 >= 256 && g.K >= 4096) return launch_wt<128, 2, 2, 2, 2>(epilogue, g, s);
+  return launch_shape<128, 128, 2, 2>(epilogue, g, s);
 }
 
 }  // namespace dlo
