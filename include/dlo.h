@@ -29,6 +29,10 @@
  *   - after a HIP error inside dlo_forward or dlo_debug_assemble the context is
  *     poisoned: every later call on it except dlo_destroy returns
  *     DLO_E_POISONED (fail closed);
+ *   - no C++ exception crosses this interface: a failed host-side allocation
+ *     inside the library returns DLO_E_HOST_OOM, and when it happens while
+ *     dlo_forward, dlo_forward_static or dlo_debug_assemble enqueues work, the
+ *     context is poisoned as after a HIP error;
  *   - a context is not thread-safe; calls on one context must not overlap.
  *
  * Data formats:
@@ -77,7 +81,7 @@ typedef int32_t dlo_status;
 #define DLO_E_INVAL (-1)     /* bad argument or configuration */
 #define DLO_E_SHAPE (-2)     /* element count or shape does not match the layout */
 #define DLO_E_STATE (-3)     /* call not valid in the context's current state */
-#define DLO_E_HOST_OOM (-4)  /* pinned host allocation failed */
+#define DLO_E_HOST_OOM (-4)  /* host allocation failed (pinned shards or the library's own bookkeeping) */
 #define DLO_E_DEV_OOM (-5)   /* the caller's device arena is too small */
 #define DLO_E_HIP (-6)       /* a HIP runtime call failed (context is poisoned) */
 #define DLO_E_POISONED (-7)  /* an earlier HIP error poisoned the context */

@@ -15,22 +15,22 @@
 namespace dlo {
 
 namespace {
-thread_local std::string g_last_error;
+// A fixed buffer, so that reporting an error never allocates (and so cannot
+// fail itself, e.g. while a host allocation failure is being reported).
+thread_local char g_last_error[512];
 }
 
 dlo_status fail(dlo_status code, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return code;
 }
 
-void clear_error() { g_last_error.clear(); }
+void clear_error() { g_last_error[0] = '\0'; }
 
-const char* last_error_cstr() { return g_last_error.c_str(); }
+const char* last_error_cstr() { return g_last_error; }
 
 dlo_status validate_block(const dlo_block_desc* b, int i) {
   if (b == nullptr) return fail(DLO_E_INVAL, "block %d: descriptor is NULL", i);
@@ -109,17 +109,19 @@ extern "C" DLO_API const char* dlo_last_error(void) { return dlo::last_error_cst
 extern "C" DLO_API dlo_status dlo_block_layout(const dlo_block_desc* block, int32_t dp_size,
                                                int64_t* numel, int64_t* shard_size,
                                                int32_t* n_params, dlo_param_desc* out, int32_t cap) {
-  dlo::clear_error();
-  if (dp_size < 1) return dlo::fail(DLO_E_INVAL, "dp_size %d must be >= 1", dp_size);
-  dlo::BlockLayout L;
-  dlo_status st = dlo::compute_layout(block, &L);
-  if (st != DLO_OK) return st;
-  if (numel) *numel = L.numel;
-  if (shard_size) *shard_size = dlo::ceil_div(L.numel, dp_size);
-  if (n_params) *n_params = L.n_params;
-  if (out) {
-    if (cap < L.n_params) return dlo::fail(DLO_E_INVAL, "cap %d < %d parameters", cap, L.n_params);
-    memcpy(out, L.params, sizeof(dlo_param_desc) * L.n_params);
-  }
-  return DLO_OK;
+  return dlo::guarded([&]() -> dlo_status {
+    dlo::clear_error();
+    if (dp_size < 1) return dlo::fail(DLO_E_INVAL, "dp_size %d must be >= 1", dp_size);
+    dlo::BlockLayout L;
+    dlo_status st = dlo::compute_layout(block, &L);
+    if (st != DLO_OK) return st;
+    if (numel) *numel = L.numel;
+    if (shard_size) *shard_size = dlo::ceil_div(L.numel, dp_size);
+    if (n_params) *n_params = L.n_params;
+    if (out) {
+      if (cap < L.n_params) return dlo::fail(DLO_E_INVAL, "cap %d < %d parameters", cap, L.n_params);
+      memcpy(out, L.params, sizeof(dlo_param_desc) * L.n_params);
+    }
+    return DLO_OK;
+  });
 }

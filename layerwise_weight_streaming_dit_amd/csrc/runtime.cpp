@@ -308,9 +308,25 @@ void copy_parallel(void* dst, const void* src, size_t bytes) {
   }
   const size_t per = (bytes + nt - 1) / nt;
   std::vector<std::thread> pool;
+  bool reserved = true;
+  try {
+    pool.reserve(nt - 1);
+  } catch (...) {
+    reserved = false;
+  }
   for (size_t t = 1; t < nt; ++t) {
     const size_t lo = t * per, n = lo < bytes ? std::min(per, bytes - lo) : 0;
-    if (n) pool.emplace_back([=] { memcpy(static_cast<char*>(dst) + lo, static_cast<const char*>(src) + lo, n); });
+    if (n == 0) continue;
+    auto piece = [=] { memcpy(static_cast<char*>(dst) + lo, static_cast<const char*>(src) + lo, n); };
+    bool started = false;
+    if (reserved) {
+      try {
+        pool.emplace_back(piece);
+        started = true;
+      } catch (...) {
+      }
+    }
+    if (!started) piece();  // no thread for this piece: copy it here
   }
   memcpy(dst, src, std::min(per, bytes));
   for (auto& th : pool) th.join();
@@ -539,140 +555,165 @@ void free_ctx(dlo_ctx* ctx) {
 
 using namespace dlo;
 
+namespace {
+
+// Entry points that enqueue GPU work: a throw part-way may leave work in
+// flight, so the context is poisoned (every later call fails closed) before
+// the exception becomes a status.
+template <class F>
+dlo_status guarded_enqueue(dlo_ctx* ctx, F&& body) noexcept {
+  return guarded([&]() -> dlo_status {
+    try {
+      return body();
+    } catch (...) {
+      if (ctx != nullptr) ctx->poisoned = true;
+      throw;
+    }
+  });
+}
+
+}  // namespace
+
 extern "C" DLO_API dlo_status dlo_required_bytes(const dlo_config* cfg, size_t* slots, size_t* landing,
                                                  size_t* workspace, size_t* total) {
-  clear_error();
-  Sizes z;
-  dlo_status st = compute_sizes(cfg, &z);
-  if (st != DLO_OK) return st;
-  if (slots) *slots = 2 * z.slot_bytes;
-  if (landing) *landing = z.landing_bytes;
-  if (workspace) *workspace = z.workspace_bytes;
-  if (total) *total = z.total;
-  return DLO_OK;
+  return guarded([&]() -> dlo_status {
+    clear_error();
+    Sizes z;
+    dlo_status st = compute_sizes(cfg, &z);
+    if (st != DLO_OK) return st;
+    if (slots) *slots = 2 * z.slot_bytes;
+    if (landing) *landing = z.landing_bytes;
+    if (workspace) *workspace = z.workspace_bytes;
+    if (total) *total = z.total;
+    return DLO_OK;
+  });
 }
 
 extern "C" DLO_API dlo_status dlo_create(const dlo_config* cfg, dlo_ctx** out) {
-  clear_error();
-  if (out == nullptr) return fail(DLO_E_INVAL, "out is NULL");
-  *out = nullptr;
-  Sizes z;
-  dlo_status st = compute_sizes(cfg, &z);
-  if (st != DLO_OK) return st;
-  if (cfg->arena == nullptr) return fail(DLO_E_INVAL, "arena is NULL");
-  if (reinterpret_cast<uintptr_t>(cfg->arena) % kAlign != 0) return fail(DLO_E_INVAL, "arena not 256-byte aligned");
-  if (cfg->arena_bytes < z.total)
-    return fail(DLO_E_DEV_OOM, "arena holds %zu bytes, %zu required", cfg->arena_bytes, z.total);
-
-  std::unique_ptr<dlo_ctx, void (*)(dlo_ctx*)> ctx(new dlo_ctx(), free_ctx);
-  ctx->device = cfg->device;
-  ctx->flags = cfg->flags;
-  ctx->dp = cfg->dp_size;
-  ctx->max_tokens = cfg->max_tokens;
-  ctx->d_max = z.d_max;
-  ctx->m_max = z.m_max;
-  ctx->mixed_width = z.mixed;
-  ctx->s_max = z.s_max;
-  ctx->chunk_elems = z.chunk;
-  ctx->slot_bytes = z.slot_bytes;
-  ctx->landing_bytes = z.landing_bytes;
-  ctx->workspace_bytes = z.workspace_bytes;
-  ctx->blocks.resize(cfg->num_blocks);
-  for (int i = 0; i < cfg->num_blocks; ++i) {
-    Block& b = ctx->blocks[i];
-    b.desc = cfg->blocks[i];
-    b.extra.assign(cfg->blocks[i].extra_len, cfg->blocks[i].extra_len + cfg->blocks[i].n_extra);
-    b.desc.extra_len = b.extra.empty() ? nullptr : b.extra.data();
-    st = compute_layout(&b.desc, &b.layout);
+  return guarded([&]() -> dlo_status {
+    clear_error();
+    if (out == nullptr) return fail(DLO_E_INVAL, "out is NULL");
+    *out = nullptr;
+    Sizes z;
+    dlo_status st = compute_sizes(cfg, &z);
     if (st != DLO_OK) return st;
-    b.shard = ceil_div(b.layout.numel, ctx->dp);
-    b.chunks = plan_chunks(ctx->dp, b.shard, b.layout.numel, ctx->chunk_elems);
-  }
-  // carve the arena: slot 0, slot 1, landing 0, landing 1, workspace
-  char* p = static_cast<char*>(cfg->arena);
-  ctx->slot[0] = reinterpret_cast<uint16_t*>(p);
-  p += z.slot_bytes;
-  ctx->slot[1] = reinterpret_cast<uint16_t*>(p);
-  p += z.slot_bytes;
-  const size_t land_one = z.landing_bytes / 2;
-  ctx->landing[0] = reinterpret_cast<uint16_t*>(p);
-  p += land_one;
-  ctx->landing[1] = reinterpret_cast<uint16_t*>(p);
-  p += land_one;
-  carve_workspace(p, size_t(cfg->max_tokens), size_t(z.d_max), size_t(z.m_max), z.mixed, &ctx->ws);
+    if (cfg->arena == nullptr) return fail(DLO_E_INVAL, "arena is NULL");
+    if (reinterpret_cast<uintptr_t>(cfg->arena) % kAlign != 0) return fail(DLO_E_INVAL, "arena not 256-byte aligned");
+    if (cfg->arena_bytes < z.total)
+      return fail(DLO_E_DEV_OOM, "arena holds %zu bytes, %zu required", cfg->arena_bytes, z.total);
 
-  DeviceGuard dg(ctx->device);
-  if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
-  dlo_ctx* c = ctx.get();
-  if (cfg->copy_stream) {
-    c->copy_s = cfg->copy_stream;
-  } else {
-    DLO_HIP(nullptr, hipStreamCreateWithFlags(&c->copy_s, hipStreamNonBlocking));
-    c->own_copy = true;
-  }
-  DLO_HIP(nullptr, hipStreamCreateWithFlags(&c->copy_s2, hipStreamNonBlocking));
-  if (cfg->gather_stream) {
-    c->gather_s = cfg->gather_stream;
-  } else {
-    DLO_HIP(nullptr, hipStreamCreateWithFlags(&c->gather_s, hipStreamNonBlocking));
-    c->own_gather = true;
-  }
-  for (int i = 0; i < 2; ++i) {
-    DLO_HIP(nullptr, hipEventCreateWithFlags(&c->h2d_done[i], hipEventDisableTiming));
-    DLO_HIP(nullptr, hipEventCreateWithFlags(&c->land_free[i], hipEventDisableTiming));
-    DLO_HIP(nullptr, hipEventCreateWithFlags(&c->asm_done[i], hipEventDisableTiming));
-    DLO_HIP(nullptr, hipEventCreateWithFlags(&c->comp_done[i], hipEventDisableTiming));
-    c->created_events = true;
-  }
-  // initial records so the first waits are satisfied
-  for (int i = 0; i < 2; ++i) {
-    DLO_HIP(nullptr, hipEventRecord(c->land_free[i], c->gather_s));
-    DLO_HIP(nullptr, hipEventRecord(c->comp_done[i], c->gather_s));
-  }
-  if (!grow_pool(c, events_per_forward(c))) return fail(DLO_E_HIP, "trace event creation failed");
-  // the device address of the library's static scratch (dlo_forward_static),
-  // taken here, at set-up, with the context's device current
-  c->static_ws_err = static_scratch(c->device, &c->static_ws);
-  if (c->static_ws_err != hipSuccess) (void)hipGetLastError();
-  DLO_HIP(nullptr, hipStreamSynchronize(c->gather_s));
-  *out = ctx.release();
-  return DLO_OK;
+    std::unique_ptr<dlo_ctx, void (*)(dlo_ctx*)> ctx(new dlo_ctx(), free_ctx);
+    ctx->device = cfg->device;
+    ctx->flags = cfg->flags;
+    ctx->dp = cfg->dp_size;
+    ctx->max_tokens = cfg->max_tokens;
+    ctx->d_max = z.d_max;
+    ctx->m_max = z.m_max;
+    ctx->mixed_width = z.mixed;
+    ctx->s_max = z.s_max;
+    ctx->chunk_elems = z.chunk;
+    ctx->slot_bytes = z.slot_bytes;
+    ctx->landing_bytes = z.landing_bytes;
+    ctx->workspace_bytes = z.workspace_bytes;
+    ctx->blocks.resize(cfg->num_blocks);
+    for (int i = 0; i < cfg->num_blocks; ++i) {
+      Block& b = ctx->blocks[i];
+      b.desc = cfg->blocks[i];
+      b.extra.assign(cfg->blocks[i].extra_len, cfg->blocks[i].extra_len + cfg->blocks[i].n_extra);
+      b.desc.extra_len = b.extra.empty() ? nullptr : b.extra.data();
+      st = compute_layout(&b.desc, &b.layout);
+      if (st != DLO_OK) return st;
+      b.shard = ceil_div(b.layout.numel, ctx->dp);
+      b.chunks = plan_chunks(ctx->dp, b.shard, b.layout.numel, ctx->chunk_elems);
+    }
+    // carve the arena: slot 0, slot 1, landing 0, landing 1, workspace
+    char* p = static_cast<char*>(cfg->arena);
+    ctx->slot[0] = reinterpret_cast<uint16_t*>(p);
+    p += z.slot_bytes;
+    ctx->slot[1] = reinterpret_cast<uint16_t*>(p);
+    p += z.slot_bytes;
+    const size_t land_one = z.landing_bytes / 2;
+    ctx->landing[0] = reinterpret_cast<uint16_t*>(p);
+    p += land_one;
+    ctx->landing[1] = reinterpret_cast<uint16_t*>(p);
+    p += land_one;
+    carve_workspace(p, size_t(cfg->max_tokens), size_t(z.d_max), size_t(z.m_max), z.mixed, &ctx->ws);
+
+    DeviceGuard dg(ctx->device);
+    if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
+    dlo_ctx* c = ctx.get();
+    if (cfg->copy_stream) {
+      c->copy_s = cfg->copy_stream;
+    } else {
+      DLO_HIP(nullptr, hipStreamCreateWithFlags(&c->copy_s, hipStreamNonBlocking));
+      c->own_copy = true;
+    }
+    DLO_HIP(nullptr, hipStreamCreateWithFlags(&c->copy_s2, hipStreamNonBlocking));
+    if (cfg->gather_stream) {
+      c->gather_s = cfg->gather_stream;
+    } else {
+      DLO_HIP(nullptr, hipStreamCreateWithFlags(&c->gather_s, hipStreamNonBlocking));
+      c->own_gather = true;
+    }
+    for (int i = 0; i < 2; ++i) {
+      DLO_HIP(nullptr, hipEventCreateWithFlags(&c->h2d_done[i], hipEventDisableTiming));
+      DLO_HIP(nullptr, hipEventCreateWithFlags(&c->land_free[i], hipEventDisableTiming));
+      DLO_HIP(nullptr, hipEventCreateWithFlags(&c->asm_done[i], hipEventDisableTiming));
+      DLO_HIP(nullptr, hipEventCreateWithFlags(&c->comp_done[i], hipEventDisableTiming));
+      c->created_events = true;
+    }
+    // initial records so the first waits are satisfied
+    for (int i = 0; i < 2; ++i) {
+      DLO_HIP(nullptr, hipEventRecord(c->land_free[i], c->gather_s));
+      DLO_HIP(nullptr, hipEventRecord(c->comp_done[i], c->gather_s));
+    }
+    if (!grow_pool(c, events_per_forward(c))) return fail(DLO_E_HIP, "trace event creation failed");
+    // the device address of the library's static scratch (dlo_forward_static),
+    // taken here, at set-up, with the context's device current
+    c->static_ws_err = static_scratch(c->device, &c->static_ws);
+    if (c->static_ws_err != hipSuccess) (void)hipGetLastError();
+    DLO_HIP(nullptr, hipStreamSynchronize(c->gather_s));
+    *out = ctx.release();
+    return DLO_OK;
+  });
 }
 
 extern "C" DLO_API dlo_status dlo_load_shards(dlo_ctx* ctx, int32_t block, const uint16_t* flat, int64_t numel) {
-  clear_error();
-  dlo_status st = check_ctx(ctx);
-  if (st != DLO_OK) return st;
-  if (block < 0 || block >= static_cast<int>(ctx->blocks.size()))
-    return fail(DLO_E_INVAL, "block %d outside [0, %zu)", block, ctx->blocks.size());
-  Block& b = ctx->blocks[block];
-  if (numel != b.layout.numel)
-    return fail(DLO_E_SHAPE, "block %d: numel %lld, layout has %lld", block, (long long)numel,
-                (long long)b.layout.numel);
-  if (flat == nullptr) return fail(DLO_E_INVAL, "flat weight is NULL");
-  DeviceGuard dg(ctx->device);
-  if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
-  // no in-flight copy may read the shards being replaced
-  DLO_HIP(ctx, hipStreamSynchronize(ctx->copy_s));
-  DLO_HIP(ctx, hipStreamSynchronize(ctx->copy_s2));
-  const int64_t S = b.shard;
-  if (b.pinned == nullptr) {
-    void* p = nullptr;
-    const size_t bytes = size_t(std::max<int64_t>(int64_t(ctx->dp) * S, 1)) * 2;
-    hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocDefault);
-    if (e != hipSuccess || p == nullptr) {
-      (void)hipGetLastError();
-      return fail(DLO_E_HOST_OOM, "block %d: pinned allocation of %zu bytes failed", block, bytes);
+  return guarded([&]() -> dlo_status {
+    clear_error();
+    dlo_status st = check_ctx(ctx);
+    if (st != DLO_OK) return st;
+    if (block < 0 || block >= static_cast<int>(ctx->blocks.size()))
+      return fail(DLO_E_INVAL, "block %d outside [0, %zu)", block, ctx->blocks.size());
+    Block& b = ctx->blocks[block];
+    if (numel != b.layout.numel)
+      return fail(DLO_E_SHAPE, "block %d: numel %lld, layout has %lld", block, (long long)numel,
+                  (long long)b.layout.numel);
+    if (flat == nullptr) return fail(DLO_E_INVAL, "flat weight is NULL");
+    DeviceGuard dg(ctx->device);
+    if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
+    // no in-flight copy may read the shards being replaced
+    DLO_HIP(ctx, hipStreamSynchronize(ctx->copy_s));
+    DLO_HIP(ctx, hipStreamSynchronize(ctx->copy_s2));
+    const int64_t S = b.shard;
+    if (b.pinned == nullptr) {
+      void* p = nullptr;
+      const size_t bytes = size_t(std::max<int64_t>(int64_t(ctx->dp) * S, 1)) * 2;
+      hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocDefault);
+      if (e != hipSuccess || p == nullptr) {
+        (void)hipGetLastError();
+        return fail(DLO_E_HOST_OOM, "block %d: pinned allocation of %zu bytes failed", block, bytes);
+      }
+      b.pinned = static_cast<uint16_t*>(p);
+      b.shards.assign(ctx->dp, nullptr);
+      for (int r = 0; r < ctx->dp; ++r) b.shards[r] = b.pinned + int64_t(r) * S;
     }
-    b.pinned = static_cast<uint16_t*>(p);
-    b.shards.assign(ctx->dp, nullptr);
-    for (int r = 0; r < ctx->dp; ++r) b.shards[r] = b.pinned + int64_t(r) * S;
-  }
-  // shard r = flat[r S, min((r + 1) S, numel)) then zeros: with the shards
-  // back to back this is the flat weight followed by the zero padding
-  copy_parallel(b.pinned, flat, size_t(numel) * 2);
-  memset(b.pinned + numel, 0, (size_t(ctx->dp) * size_t(S) - size_t(numel)) * 2);
-  return DLO_OK;
+    // shard r = flat[r S, min((r + 1) S, numel)) then zeros: with the shards
+    // back to back this is the flat weight followed by the zero padding
+    copy_parallel(b.pinned, flat, size_t(numel) * 2);
+    memset(b.pinned + numel, 0, (size_t(ctx->dp) * size_t(S) - size_t(numel)) * 2);
+    return DLO_OK;
+  });
 }
 
 namespace dlo {
@@ -746,102 +787,114 @@ dlo_status forward_impl(dlo_ctx* ctx, float* x, const float* cond, int32_t token
 
 extern "C" DLO_API dlo_status dlo_forward(dlo_ctx* ctx, float* x, const float* cond, int32_t tokens,
                                           hipStream_t stream) {
-  clear_error();
-  dlo_status st = check_forward(ctx, x, cond, tokens);
-  if (st == DLO_OK) st = check_loaded(ctx);
-  if (st != DLO_OK) return st;
-  return forward_impl(ctx, x, cond, tokens, stream, ctx->ws);
+  return guarded_enqueue(ctx, [&]() -> dlo_status {
+    clear_error();
+    dlo_status st = check_forward(ctx, x, cond, tokens);
+    if (st == DLO_OK) st = check_loaded(ctx);
+    if (st != DLO_OK) return st;
+    return forward_impl(ctx, x, cond, tokens, stream, ctx->ws);
+  });
 }
 
 extern "C" DLO_API dlo_status dlo_forward_static(dlo_ctx* ctx, float* x, const float* cond, int32_t tokens,
                                                  hipStream_t stream) {
-  clear_error();
-  dlo_status st = check_forward(ctx, x, cond, tokens);
-  if (st != DLO_OK) return st;
-  const size_t need = carve_workspace(nullptr, size_t(tokens), size_t(ctx->d_max), size_t(ctx->m_max),
-                                      ctx->mixed_width, nullptr);
-  if (need > kStaticScratchBytes)
-    return fail(DLO_E_INVAL, "%d tokens need %zu bytes of activation workspace; the static scratch holds %zu",
-                tokens, need, kStaticScratchBytes);
-  if (ctx->flags & (DLO_FLAG_TRACE | DLO_FLAG_TRACE_KERNELS))
-    return fail(DLO_E_STATE, "tracing creates timing events; clear the trace flags for dlo_forward_static");
-  if (ctx->static_ws == nullptr)
-    return fail(DLO_E_STATE, "the static scratch is unavailable on device %d: %s", ctx->device,
-                hipGetErrorString(ctx->static_ws_err));
-  st = check_loaded(ctx);
-  if (st != DLO_OK) return st;
-  Workspace w;
-  carve_workspace(static_cast<char*>(ctx->static_ws), size_t(tokens), size_t(ctx->d_max), size_t(ctx->m_max),
-                  ctx->mixed_width, &w);
-  return forward_impl(ctx, x, cond, tokens, stream, w);
+  return guarded_enqueue(ctx, [&]() -> dlo_status {
+    clear_error();
+    dlo_status st = check_forward(ctx, x, cond, tokens);
+    if (st != DLO_OK) return st;
+    const size_t need = carve_workspace(nullptr, size_t(tokens), size_t(ctx->d_max), size_t(ctx->m_max),
+                                        ctx->mixed_width, nullptr);
+    if (need > kStaticScratchBytes)
+      return fail(DLO_E_INVAL, "%d tokens need %zu bytes of activation workspace; the static scratch holds %zu",
+                  tokens, need, kStaticScratchBytes);
+    if (ctx->flags & (DLO_FLAG_TRACE | DLO_FLAG_TRACE_KERNELS))
+      return fail(DLO_E_STATE, "tracing creates timing events; clear the trace flags for dlo_forward_static");
+    if (ctx->static_ws == nullptr)
+      return fail(DLO_E_STATE, "the static scratch is unavailable on device %d: %s", ctx->device,
+                  hipGetErrorString(ctx->static_ws_err));
+    st = check_loaded(ctx);
+    if (st != DLO_OK) return st;
+    Workspace w;
+    carve_workspace(static_cast<char*>(ctx->static_ws), size_t(tokens), size_t(ctx->d_max), size_t(ctx->m_max),
+                    ctx->mixed_width, &w);
+    return forward_impl(ctx, x, cond, tokens, stream, w);
+  });
 }
 
 extern "C" DLO_API dlo_status dlo_destroy(dlo_ctx* ctx) {
-  clear_error();
-  if (ctx == nullptr) return DLO_OK;
-  {
-    DeviceGuard dg(ctx->device);
-    if (!ctx->poisoned) {
-      (void)hipStreamSynchronize(ctx->copy_s);
-      (void)hipStreamSynchronize(ctx->copy_s2);
-      (void)hipStreamSynchronize(ctx->gather_s);
-      (void)hipEventSynchronize(ctx->comp_done[0]);
-      (void)hipEventSynchronize(ctx->comp_done[1]);
+  return guarded([&]() -> dlo_status {
+    clear_error();
+    if (ctx == nullptr) return DLO_OK;
+    {
+      DeviceGuard dg(ctx->device);
+      if (!ctx->poisoned) {
+        (void)hipStreamSynchronize(ctx->copy_s);
+        (void)hipStreamSynchronize(ctx->copy_s2);
+        (void)hipStreamSynchronize(ctx->gather_s);
+        (void)hipEventSynchronize(ctx->comp_done[0]);
+        (void)hipEventSynchronize(ctx->comp_done[1]);
+      }
     }
-  }
-  free_ctx(ctx);
-  return DLO_OK;
+    free_ctx(ctx);
+    return DLO_OK;
+  });
 }
 
 extern "C" DLO_API dlo_status dlo_layout(dlo_ctx* ctx, int32_t block, int64_t* numel, int64_t* shard_size,
                                          int32_t* n_params, dlo_param_desc* out, int32_t cap) {
-  clear_error();
-  if (ctx == nullptr) return fail(DLO_E_INVAL, "context is NULL");
-  if (block < 0 || block >= static_cast<int>(ctx->blocks.size()))
-    return fail(DLO_E_INVAL, "block %d outside [0, %zu)", block, ctx->blocks.size());
-  const Block& b = ctx->blocks[block];
-  if (numel) *numel = b.layout.numel;
-  if (shard_size) *shard_size = b.shard;
-  if (n_params) *n_params = b.layout.n_params;
-  if (out) {
-    if (cap < b.layout.n_params) return fail(DLO_E_INVAL, "cap %d < %d parameters", cap, b.layout.n_params);
-    memcpy(out, b.layout.params, sizeof(dlo_param_desc) * b.layout.n_params);
-  }
-  return DLO_OK;
+  return guarded([&]() -> dlo_status {
+    clear_error();
+    if (ctx == nullptr) return fail(DLO_E_INVAL, "context is NULL");
+    if (block < 0 || block >= static_cast<int>(ctx->blocks.size()))
+      return fail(DLO_E_INVAL, "block %d outside [0, %zu)", block, ctx->blocks.size());
+    const Block& b = ctx->blocks[block];
+    if (numel) *numel = b.layout.numel;
+    if (shard_size) *shard_size = b.shard;
+    if (n_params) *n_params = b.layout.n_params;
+    if (out) {
+      if (cap < b.layout.n_params) return fail(DLO_E_INVAL, "cap %d < %d parameters", cap, b.layout.n_params);
+      memcpy(out, b.layout.params, sizeof(dlo_param_desc) * b.layout.n_params);
+    }
+    return DLO_OK;
+  });
 }
 
 extern "C" DLO_API dlo_status dlo_get_shard(dlo_ctx* ctx, int32_t block, int32_t rank, const uint16_t** ptr,
                                             int64_t* n) {
-  clear_error();
-  if (ctx == nullptr || ptr == nullptr || n == nullptr) return fail(DLO_E_INVAL, "NULL argument");
-  if (block < 0 || block >= static_cast<int>(ctx->blocks.size()))
-    return fail(DLO_E_INVAL, "block %d outside [0, %zu)", block, ctx->blocks.size());
-  if (rank < 0 || rank >= ctx->dp) return fail(DLO_E_INVAL, "rank %d outside [0, %d)", rank, ctx->dp);
-  const Block& b = ctx->blocks[block];
-  if (b.shards.empty()) return fail(DLO_E_STATE, "block %d has no shards loaded", block);
-  *ptr = b.shards[rank];
-  *n = b.shard;
-  return DLO_OK;
+  return guarded([&]() -> dlo_status {
+    clear_error();
+    if (ctx == nullptr || ptr == nullptr || n == nullptr) return fail(DLO_E_INVAL, "NULL argument");
+    if (block < 0 || block >= static_cast<int>(ctx->blocks.size()))
+      return fail(DLO_E_INVAL, "block %d outside [0, %zu)", block, ctx->blocks.size());
+    if (rank < 0 || rank >= ctx->dp) return fail(DLO_E_INVAL, "rank %d outside [0, %d)", rank, ctx->dp);
+    const Block& b = ctx->blocks[block];
+    if (b.shards.empty()) return fail(DLO_E_STATE, "block %d has no shards loaded", block);
+    *ptr = b.shards[rank];
+    *n = b.shard;
+    return DLO_OK;
+  });
 }
 
 extern "C" DLO_API dlo_status dlo_debug_assemble(dlo_ctx* ctx, int32_t block, uint16_t* host_out, int64_t cap) {
-  clear_error();
-  dlo_status st = check_ctx(ctx);
-  if (st != DLO_OK) return st;
-  if (block < 0 || block >= static_cast<int>(ctx->blocks.size()))
-    return fail(DLO_E_INVAL, "block %d outside [0, %zu)", block, ctx->blocks.size());
-  Block& b = ctx->blocks[block];
-  if (b.shards.empty()) return fail(DLO_E_STATE, "block %d has no shards loaded", block);
-  if (host_out == nullptr || cap < b.layout.numel)
-    return fail(DLO_E_INVAL, "host_out must hold %lld elements", (long long)b.layout.numel);
-  DeviceGuard dg(ctx->device);
-  if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
-  const int k = block & 1;  // either slot: the staging waits until no compute reads it
-  st = enqueue_staging(ctx, block, k, false, false);
-  if (st != DLO_OK) return st;
-  DLO_HIP(ctx, hipStreamSynchronize(ctx->gather_s));
-  DLO_HIP(ctx, hipMemcpy(host_out, ctx->slot[k], size_t(b.layout.numel) * 2, hipMemcpyDeviceToHost));
-  return DLO_OK;
+  return guarded_enqueue(ctx, [&]() -> dlo_status {
+    clear_error();
+    dlo_status st = check_ctx(ctx);
+    if (st != DLO_OK) return st;
+    if (block < 0 || block >= static_cast<int>(ctx->blocks.size()))
+      return fail(DLO_E_INVAL, "block %d outside [0, %zu)", block, ctx->blocks.size());
+    Block& b = ctx->blocks[block];
+    if (b.shards.empty()) return fail(DLO_E_STATE, "block %d has no shards loaded", block);
+    if (host_out == nullptr || cap < b.layout.numel)
+      return fail(DLO_E_INVAL, "host_out must hold %lld elements", (long long)b.layout.numel);
+    DeviceGuard dg(ctx->device);
+    if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
+    const int k = block & 1;  // either slot: the staging waits until no compute reads it
+    st = enqueue_staging(ctx, block, k, false, false);
+    if (st != DLO_OK) return st;
+    DLO_HIP(ctx, hipStreamSynchronize(ctx->gather_s));
+    DLO_HIP(ctx, hipMemcpy(host_out, ctx->slot[k], size_t(b.layout.numel) * 2, hipMemcpyDeviceToHost));
+    return DLO_OK;
+  });
 }
 
 namespace {
@@ -998,78 +1051,88 @@ dlo_status collect_trace(dlo_ctx* ctx, std::vector<dlo_interval>& out, dlo_stats
 }  // namespace
 
 extern "C" DLO_API dlo_status dlo_get_stats(dlo_ctx* ctx, dlo_stats* out) {
-  clear_error();
-  dlo_status st = check_ctx(ctx);
-  if (st != DLO_OK) return st;
-  if (out == nullptr) return fail(DLO_E_INVAL, "out is NULL");
-  DeviceGuard dg(ctx->device);
-  memset(out, 0, sizeof(*out));
-  out->num_blocks = static_cast<int32_t>(ctx->blocks.size());
-  out->dp_size = ctx->dp;
-  out->forwards = ctx->forwards;
-  out->max_shard_elems = ctx->s_max;
-  out->slot_bytes = ctx->slot_bytes;
-  out->landing_bytes = ctx->landing_bytes;
-  out->workspace_bytes = ctx->workspace_bytes;
-  int64_t hb = 0;
-  for (auto& b : ctx->blocks) hb += int64_t(2) * ctx->dp * b.shard;
-  out->h2d_bytes_per_forward = hb;
-  out->landing_chunk_elems = ctx->chunk_elems;
-  out->max_block_bytes = size_t(2) * size_t(ctx->dp) * size_t(ctx->s_max);
-  out->weight_bytes_allocated = 2 * ctx->slot_bytes + ctx->landing_bytes;
-  std::vector<dlo_interval> tmp;
-  return collect_trace(ctx, tmp, out);
+  return guarded([&]() -> dlo_status {
+    clear_error();
+    dlo_status st = check_ctx(ctx);
+    if (st != DLO_OK) return st;
+    if (out == nullptr) return fail(DLO_E_INVAL, "out is NULL");
+    DeviceGuard dg(ctx->device);
+    memset(out, 0, sizeof(*out));
+    out->num_blocks = static_cast<int32_t>(ctx->blocks.size());
+    out->dp_size = ctx->dp;
+    out->forwards = ctx->forwards;
+    out->max_shard_elems = ctx->s_max;
+    out->slot_bytes = ctx->slot_bytes;
+    out->landing_bytes = ctx->landing_bytes;
+    out->workspace_bytes = ctx->workspace_bytes;
+    int64_t hb = 0;
+    for (auto& b : ctx->blocks) hb += int64_t(2) * ctx->dp * b.shard;
+    out->h2d_bytes_per_forward = hb;
+    out->landing_chunk_elems = ctx->chunk_elems;
+    out->max_block_bytes = size_t(2) * size_t(ctx->dp) * size_t(ctx->s_max);
+    out->weight_bytes_allocated = 2 * ctx->slot_bytes + ctx->landing_bytes;
+    std::vector<dlo_interval> tmp;
+    return collect_trace(ctx, tmp, out);
+  });
 }
 
 extern "C" DLO_API dlo_status dlo_get_trace(dlo_ctx* ctx, dlo_interval* out, int32_t cap, int32_t* n) {
-  clear_error();
-  dlo_status st = check_ctx(ctx);
-  if (st != DLO_OK) return st;
-  if (n == nullptr) return fail(DLO_E_INVAL, "n is NULL");
-  DeviceGuard dg(ctx->device);
-  std::vector<dlo_interval> tmp;
-  st = collect_trace(ctx, tmp, nullptr);
-  if (st != DLO_OK) return st;
-  *n = static_cast<int32_t>(tmp.size());
-  if (out) {
-    if (cap < *n) return fail(DLO_E_INVAL, "cap %d < %d intervals", cap, *n);
-    memcpy(out, tmp.data(), sizeof(dlo_interval) * tmp.size());
-    // accumulating traces (kernel-only, or spanning forwards) are consumed
-    if (!(ctx->flags & DLO_FLAG_TRACE) || (ctx->flags & DLO_FLAG_TRACE_SPAN)) drop_trace(ctx);
-  }
-  return DLO_OK;
+  return guarded([&]() -> dlo_status {
+    clear_error();
+    dlo_status st = check_ctx(ctx);
+    if (st != DLO_OK) return st;
+    if (n == nullptr) return fail(DLO_E_INVAL, "n is NULL");
+    DeviceGuard dg(ctx->device);
+    std::vector<dlo_interval> tmp;
+    st = collect_trace(ctx, tmp, nullptr);
+    if (st != DLO_OK) return st;
+    *n = static_cast<int32_t>(tmp.size());
+    if (out) {
+      if (cap < *n) return fail(DLO_E_INVAL, "cap %d < %d intervals", cap, *n);
+      memcpy(out, tmp.data(), sizeof(dlo_interval) * tmp.size());
+      // accumulating traces (kernel-only, or spanning forwards) are consumed
+      if (!(ctx->flags & DLO_FLAG_TRACE) || (ctx->flags & DLO_FLAG_TRACE_SPAN)) drop_trace(ctx);
+    }
+    return DLO_OK;
+  });
 }
 
 extern "C" DLO_API dlo_status dlo_set_flags(dlo_ctx* ctx, uint32_t flags) {
-  clear_error();
-  dlo_status st = check_ctx(ctx);
-  if (st != DLO_OK) return st;
-  constexpr uint32_t kKnown = DLO_FLAG_TRACE | DLO_FLAG_SERIALIZE | DLO_FLAG_POISON_SLOTS |
-                              DLO_FLAG_TRACE_KERNELS | DLO_FLAG_TRACE_SPAN;
-  if (flags & ~kKnown) return fail(DLO_E_INVAL, "unknown flags 0x%x", flags & ~kKnown);
-  ctx->flags = flags;
-  drop_trace(ctx);
-  return DLO_OK;
+  return guarded([&]() -> dlo_status {
+    clear_error();
+    dlo_status st = check_ctx(ctx);
+    if (st != DLO_OK) return st;
+    constexpr uint32_t kKnown = DLO_FLAG_TRACE | DLO_FLAG_SERIALIZE | DLO_FLAG_POISON_SLOTS |
+                                DLO_FLAG_TRACE_KERNELS | DLO_FLAG_TRACE_SPAN;
+    if (flags & ~kKnown) return fail(DLO_E_INVAL, "unknown flags 0x%x", flags & ~kKnown);
+    ctx->flags = flags;
+    drop_trace(ctx);
+    return DLO_OK;
+  });
 }
 
 extern "C" DLO_API dlo_status dlo_set_trace_kinds(dlo_ctx* ctx, uint32_t kinds) {
-  clear_error();
-  dlo_status st = check_ctx(ctx);
-  if (st != DLO_OK) return st;
-  if (kinds & ~DLO_TRACE_KINDS_ALL) return fail(DLO_E_INVAL, "unknown interval kinds 0x%x", kinds & ~DLO_TRACE_KINDS_ALL);
-  ctx->trace_kinds = kinds;
-  drop_trace(ctx);
-  return DLO_OK;
+  return guarded([&]() -> dlo_status {
+    clear_error();
+    dlo_status st = check_ctx(ctx);
+    if (st != DLO_OK) return st;
+    if (kinds & ~DLO_TRACE_KINDS_ALL) return fail(DLO_E_INVAL, "unknown interval kinds 0x%x", kinds & ~DLO_TRACE_KINDS_ALL);
+    ctx->trace_kinds = kinds;
+    drop_trace(ctx);
+    return DLO_OK;
+  });
 }
 
 extern "C" DLO_API dlo_status dlo_reserve_trace(dlo_ctx* ctx, int32_t forwards) {
-  clear_error();
-  dlo_status st = check_ctx(ctx);
-  if (st != DLO_OK) return st;
-  if (forwards < 0) return fail(DLO_E_INVAL, "forwards %d < 0", forwards);
-  DeviceGuard dg(ctx->device);
-  if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
-  const size_t want = ctx->ev_next + size_t(forwards) * events_per_forward(ctx);
-  if (!grow_pool(ctx, want)) return fail(DLO_E_HIP, "trace event creation failed");
-  return DLO_OK;
+  return guarded([&]() -> dlo_status {
+    clear_error();
+    dlo_status st = check_ctx(ctx);
+    if (st != DLO_OK) return st;
+    if (forwards < 0) return fail(DLO_E_INVAL, "forwards %d < 0", forwards);
+    DeviceGuard dg(ctx->device);
+    if (!dg.ok) return fail(DLO_E_HIP, "hipSetDevice(%d) failed", ctx->device);
+    const size_t want = ctx->ev_next + size_t(forwards) * events_per_forward(ctx);
+    if (!grow_pool(ctx, want)) return fail(DLO_E_HIP, "trace event creation failed");
+    return DLO_OK;
+  });
 }

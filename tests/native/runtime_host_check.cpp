@@ -20,6 +20,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <new>
 #include <vector>
 
 #include "dlo.h"
@@ -37,6 +38,8 @@ namespace {
 double g_clock = 0;       // logical time, one unit per enqueued operation
 int g_memcpy_calls = 0;   // hipMemcpyAsync calls so far
 int g_fail_memcpy_at = -1;  // make that call fail (fail-closed test)
+int g_gemm_calls = 0;       // launch_gemm calls so far
+int g_throw_gemm_at = -1;   // make that call throw std::bad_alloc (exception test)
 int g_streams = 0;
 }  // namespace
 
@@ -181,6 +184,7 @@ hipError_t launch_ln_modulate(const float*, int, float*, const float*, const flo
 }
 
 hipError_t launch_gemm(int epilogue, const GemmArgs& g, hipStream_t) {
+  if (g_gemm_calls++ == g_throw_gemm_at) throw std::bad_alloc();
   // the weight operand: `a` for the transposed v projection, `w` otherwise
   const uint16_t* wt = epilogue == EPI_VT_F16 ? g.a : g.w;
   const char* name = "W1";
@@ -448,6 +452,23 @@ void run_fail_closed_case() {
   destroy(c);
 }
 
+// A C++ exception inside the library (here a host allocation failure in the
+// middle of a forward's enqueue) comes back as DLO_E_HOST_OOM with a message,
+// not as an exception through the C ABI, and poisons the context, since work
+// may already be in flight.
+void run_exception_case() {
+  Ctx c;
+  std::vector<dlo_block_desc> descs(3, dlo_block_desc{128, 2, 256, 64, 0, 0, nullptr});
+  CHECK(make(c, descs, 2, 8, 4096, 0) == DLO_OK);
+  if (!c.ctx) return;
+  g_throw_gemm_at = g_gemm_calls + 7;
+  CHECK(dlo_forward(c.ctx, c.x.data(), c.cond.data(), 8, nullptr) == DLO_E_HOST_OOM);
+  g_throw_gemm_at = -1;
+  CHECK(strstr(dlo_last_error(), "allocation failed") != nullptr);
+  CHECK(dlo_forward(c.ctx, c.x.data(), c.cond.data(), 8, nullptr) == DLO_E_POISONED);
+  destroy(c);
+}
+
 }  // namespace
 
 int main() {
@@ -465,6 +486,7 @@ int main() {
   run_schedule_case({wide}, 1, 4096, DLO_FLAG_POISON_SLOTS);
   run_trace_kinds_case();
   run_fail_closed_case();
+  run_exception_case();
   if (g_failures) {
     fprintf(stderr, "%d check(s) failed\n", g_failures);
     return 1;
