@@ -387,6 +387,14 @@ hipEvent_t next_ev(dlo_ctx* ctx) {
   return ctx->ev_pool[ctx->ev_next++];
 }
 
+// The start/end events of one traced interval: both, or neither (the
+// interval is then skipped) when the pool cannot supply two.
+void take_event_pair(dlo_ctx* ctx, TraceEv* t) {
+  t->start = next_ev(ctx);
+  t->end = t->start ? next_ev(ctx) : nullptr;
+  if (t->end == nullptr) t->start = nullptr;
+}
+
 // Enqueue the H2D + reconstruction of block b into slot k on the copy and
 // gather streams.  `trace` adds timed intervals; `in_forward` is false for
 // the stand-alone debug path (no compute of block b-1 to wait for).
@@ -413,7 +421,8 @@ dlo_status enqueue_staging(dlo_ctx* ctx, int b, int k, bool trace, bool in_forwa
     }
     TraceEv tv{};
     if (trace && traced(ctx, DLO_IV_H2D)) {
-      tv = TraceEv{DLO_IV_H2D, b, static_cast<int>(ci), -1, lb, fwd_index(ctx), c.len * 2, next_ev(ctx), next_ev(ctx)};
+      tv = TraceEv{DLO_IV_H2D, b, static_cast<int>(ci), -1, lb, fwd_index(ctx), c.len * 2, nullptr, nullptr};
+      take_event_pair(ctx, &tv);
       if (tv.start) DLO_HIP(ctx, hipEventRecord(tv.start, cs));
     }
     DLO_HIP(ctx, hipMemcpyAsync(land, blk.pinned + c.off, size_t(c.len) * 2, hipMemcpyHostToDevice, cs));
@@ -431,7 +440,8 @@ dlo_status enqueue_staging(dlo_ctx* ctx, int b, int k, bool trace, bool in_forwa
     DLO_HIP(ctx, hipStreamWaitEvent(ctx->gather_s, ctx->h2d_done[lb], 0));
     TraceEv ta{};
     if (trace && traced(ctx, DLO_IV_ASM)) {
-      ta = TraceEv{DLO_IV_ASM, b, static_cast<int>(ci), k, lb, fwd_index(ctx), c.valid * 2, next_ev(ctx), next_ev(ctx)};
+      ta = TraceEv{DLO_IV_ASM, b, static_cast<int>(ci), k, lb, fwd_index(ctx), c.valid * 2, nullptr, nullptr};
+      take_event_pair(ctx, &ta);
       if (ta.start) DLO_HIP(ctx, hipEventRecord(ta.start, ctx->gather_s));
     }
     DLO_HIP(ctx, launch_assemble(ctx->slot[k] + c.off, land, c.valid, ctx->gather_s));
@@ -471,7 +481,8 @@ dlo_status enqueue_block_compute(dlo_ctx* ctx, int b, int k, float*& x_cur, int&
   auto timed = [&](int kind, auto&& launch) -> dlo_status {
     TraceEv tv{};
     if (trace && traced(ctx, kind)) {
-      tv = TraceEv{kind, b, -1, k, -1, fwd_index(ctx), 0, next_ev(ctx), next_ev(ctx)};
+      tv = TraceEv{kind, b, -1, k, -1, fwd_index(ctx), 0, nullptr, nullptr};
+      take_event_pair(ctx, &tv);
       if (tv.start) DLO_HIP(ctx, hipEventRecord(tv.start, s));
     }
     DLO_HIP(ctx, launch());
@@ -763,7 +774,8 @@ dlo_status forward_impl(dlo_ctx* ctx, float* x, const float* cond, int32_t token
     DLO_HIP(ctx, hipStreamWaitEvent(stream, ctx->asm_done[k], 0));
     TraceEv tc{};
     if (trace && traced(ctx, DLO_IV_COMPUTE)) {
-      tc = TraceEv{DLO_IV_COMPUTE, b, -1, k, -1, fwd_index(ctx), 0, next_ev(ctx), next_ev(ctx)};
+      tc = TraceEv{DLO_IV_COMPUTE, b, -1, k, -1, fwd_index(ctx), 0, nullptr, nullptr};
+      take_event_pair(ctx, &tc);
       if (tc.start) DLO_HIP(ctx, hipEventRecord(tc.start, stream));
     }
     st = enqueue_block_compute(ctx, b, k, x_cur, d_cur, x, cond, tokens, stream, trace, w);

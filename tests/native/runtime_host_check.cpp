@@ -39,12 +39,15 @@ double g_clock = 0;       // logical time, one unit per enqueued operation
 int g_memcpy_calls = 0;   // hipMemcpyAsync calls so far
 int g_fail_memcpy_at = -1;  // make that call fail (fail-closed test)
 int g_gemm_calls = 0;       // launch_gemm calls so far
+int g_event_creates = 0;    // hipEventCreate calls so far
+int g_fail_event_create_at = -1;  // make that call fail (trace event test)
 int g_throw_gemm_at = -1;   // make that call throw std::bad_alloc (exception test)
 int g_streams = 0;
 }  // namespace
 
 extern "C" {
 hipError_t hipEventCreate(hipEvent_t* e) {
+  if (g_event_creates++ == g_fail_event_create_at) return hipErrorInvalidValue;
   *e = new ihipEvent_t{0};
   return hipSuccess;
 }
@@ -452,6 +455,30 @@ void run_fail_closed_case() {
   destroy(c);
 }
 
+// A trace event that cannot be created skips its interval: the forward and
+// the trace read still succeed, and every interval read has both ends.
+// Kernel-only tracing accumulates over forwards, so the second forward grows
+// the event pool, two creations per interval (start, end); the creation of
+// its second interval's start event fails.
+void run_trace_event_failure_case() {
+  Ctx c;
+  std::vector<dlo_block_desc> descs(3, dlo_block_desc{128, 2, 256, 64, 0, 0, nullptr});
+  CHECK(make(c, descs, 2, 8, 0, DLO_FLAG_TRACE_KERNELS) == DLO_OK);
+  if (!c.ctx) return;
+  CHECK(dlo_forward(c.ctx, c.x.data(), c.cond.data(), 8, nullptr) == DLO_OK);
+  g_fail_event_create_at = g_event_creates + 2;
+  CHECK(dlo_forward(c.ctx, c.x.data(), c.cond.data(), 8, nullptr) == DLO_OK);
+  CHECK(g_event_creates > g_fail_event_create_at);  // the failing creation happened
+  g_fail_event_create_at = -1;
+  int32_t n = 0;
+  CHECK(dlo_get_trace(c.ctx, nullptr, 0, &n) == DLO_OK);
+  CHECK(n == 2 * 3 * 10 - 1);  // per block: the compute interval and nine kernels
+  std::vector<dlo_interval> iv(n > 0 ? n : 0);
+  CHECK(dlo_get_trace(c.ctx, iv.data(), n, &n) == DLO_OK);
+  for (auto& v : iv) CHECK(v.end_ms >= v.start_ms);
+  destroy(c);
+}
+
 // A C++ exception inside the library (here a host allocation failure in the
 // middle of a forward's enqueue) comes back as DLO_E_HOST_OOM with a message,
 // not as an exception through the C ABI, and poisons the context, since work
@@ -487,6 +514,7 @@ int main() {
   run_trace_kinds_case();
   run_fail_closed_case();
   run_exception_case();
+  run_trace_event_failure_case();
   if (g_failures) {
     fprintf(stderr, "%d check(s) failed\n", g_failures);
     return 1;
