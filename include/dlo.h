@@ -316,7 +316,8 @@ DLO_API dlo_status dlo_forward_static(dlo_ctx* ctx, float* x, const float* cond,
 
 /* Tear the context down (release page, section "Double-buffered prefetch":
  * the buffers live as long as the model).  Synchronises the context's
- * streams, frees pinned shards, events and owned streams.  The arena returns
+ * streams (also on a poisoned context, whose work may still be in flight),
+ * frees pinned shards, events and owned streams.  The arena returns
  * to the caller.  NULL is a no-op.  Always returns DLO_OK. */
 DLO_API dlo_status dlo_destroy(dlo_ctx* ctx);
 

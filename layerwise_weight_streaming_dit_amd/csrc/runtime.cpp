@@ -838,14 +838,18 @@ extern "C" DLO_API dlo_status dlo_destroy(dlo_ctx* ctx) {
     clear_error();
     if (ctx == nullptr) return DLO_OK;
     {
+      // Wait for every enqueued copy, reconstruction and block before the
+      // pinned shards are freed and the caller releases the arena -- also on
+      // a poisoned context: a host allocation failure poisons one with work
+      // in flight on a healthy device, and after a device fault these calls
+      // return the fault at once.
       DeviceGuard dg(ctx->device);
-      if (!ctx->poisoned) {
-        (void)hipStreamSynchronize(ctx->copy_s);
-        (void)hipStreamSynchronize(ctx->copy_s2);
-        (void)hipStreamSynchronize(ctx->gather_s);
-        (void)hipEventSynchronize(ctx->comp_done[0]);
-        (void)hipEventSynchronize(ctx->comp_done[1]);
-      }
+      (void)hipStreamSynchronize(ctx->copy_s);
+      (void)hipStreamSynchronize(ctx->copy_s2);
+      (void)hipStreamSynchronize(ctx->gather_s);
+      (void)hipEventSynchronize(ctx->comp_done[0]);
+      (void)hipEventSynchronize(ctx->comp_done[1]);
+      (void)hipGetLastError();
     }
     free_ctx(ctx);
     return DLO_OK;
