@@ -242,6 +242,16 @@ class StreamedDiT:
         return int(numel.value), int(shard.value), [
             (p.name.decode(), int(p.offset), tuple(int(p.shape[i]) for i in range(p.ndim))) for p in out[: n.value]]
 
+    def pinned_bytes(self) -> int:
+        """Pinned host bytes holding the loaded blocks' shards (dp_size shards
+        of ceil(numel / dp_size) elements per block, 2 bytes each)."""
+        total = 0
+        for b in range(len(self.shapes)):
+            ptr, n = _P(), _I64()
+            if lib().dlo_get_shard(self._h, b, 0, ctypes.byref(ptr), ctypes.byref(n)) == OK and ptr.value:
+                total += self.dp_size * int(n.value) * 2
+        return total
+
     def get_shard(self, block: int, rank: int) -> np.ndarray:
         ptr, n = _P(), _I64()
         check(lib().dlo_get_shard(self._h, block, rank, ctypes.byref(ptr), ctypes.byref(n)))

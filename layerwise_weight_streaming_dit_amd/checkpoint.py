@@ -149,13 +149,25 @@ def read_block(path: str, shapes: Sequence, b: int) -> np.ndarray:
 
 def host_memory() -> Dict[str, int]:
     """This process's resident memory in bytes (Linux /proc): RSS, its
-    anonymous and file-backed parts, and the peak RSS."""
+    anonymous and file-backed parts and the peak RSS, and the proportional
+    set size (PSS: each shared page divided among the processes mapping it,
+    so a checkpoint's page cache mapped by several processes is counted
+    once overall) with its anonymous and file-backed parts, where the kernel
+    provides smaps_rollup."""
     out = {}
     with open("/proc/self/status") as f:
         for line in f:
             k, _, v = line.partition(":")
             if k in ("VmRSS", "RssAnon", "RssFile", "RssShmem", "VmHWM"):
                 out[k] = int(v.split()[0]) * 1024
+    try:
+        with open("/proc/self/smaps_rollup") as f:
+            for line in f:
+                k, _, v = line.partition(":")
+                if k in ("Pss", "Pss_Anon", "Pss_File"):
+                    out[k] = int(v.split()[0]) * 1024
+    except OSError:
+        pass
     return out
 
 

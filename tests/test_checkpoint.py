@@ -103,3 +103,20 @@ def test_wrong_block_count_rejected(tmp_path):
         C.plan(path, shapes + [shapes[0]])
     with pytest.raises(ValueError, match="not in the block layout"):
         C.plan(path, shapes[:1])
+
+
+def test_host_memory_reports_rss_and_pss():
+    """The resident-memory figures the checkpoint test reports: RSS and its
+    parts from /proc/self/status, PSS and its parts from smaps_rollup; a new
+    anonymous 64 MiB region, once touched, shows up in both anonymous sums."""
+    m0 = C.host_memory()
+    for k in ("VmRSS", "RssAnon", "RssFile"):
+        assert m0[k] > 0
+    if "Pss" not in m0:
+        pytest.skip("no /proc/self/smaps_rollup on this kernel")
+    assert 0 < m0["Pss"] <= m0["VmRSS"]
+    buf = np.ones(64 << 20, dtype=np.uint8)
+    m1 = C.host_memory()
+    assert m1["RssAnon"] - m0["RssAnon"] >= (60 << 20)
+    assert m1["Pss_Anon"] - m0["Pss_Anon"] >= (60 << 20)
+    del buf

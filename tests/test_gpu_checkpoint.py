@@ -52,6 +52,16 @@ def test_mmap_load_matches_in_memory_load_without_a_host_copy(tmp_path):
     print(f"[mmap] anonymous RSS growth: mmap load {grow_mmap / 1e6:.1f} MB, in-memory load "
           f"{grow_mem / 1e6:.1f} MB (model {model_bytes / 1e6:.1f} MB); file-backed RSS after the mmap "
           f"load {(m1['RssFile'] - m0['RssFile']) / 1e6:.1f} MB", flush=True)
+    if "Pss" in m0:
+        print(f"[mmap] PSS growth: mmap load {(m1['Pss'] - m0['Pss']) / 1e6:.1f} MB (anonymous "
+              f"{(m1['Pss_Anon'] - m0['Pss_Anon']) / 1e6:.1f}, file {(m1['Pss_File'] - m0['Pss_File']) / 1e6:.1f}), "
+              f"in-memory load {(m2['Pss'] - m1['Pss']) / 1e6:.1f} MB (anonymous "
+              f"{(m2['Pss_Anon'] - m1['Pss_Anon']) / 1e6:.1f})", flush=True)
+    # pinned shard bytes: dp shards of ceil(numel / dp) elements per block, in
+    # both contexts, whichever way the weights were read
+    pinned = sum(dp * -(-n // dp) * 2 for n in numels)
+    print(f"[mmap] pinned shard bytes per context: {pinned / 1e6:.1f} MB", flush=True)
+    assert a.pinned_bytes() == b.pinned_bytes() == pinned
     # the in-memory path holds one more anonymous copy of the model than the mmap path
     assert grow_mem - grow_mmap >= 0.9 * model_bytes
 
